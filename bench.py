@@ -1,0 +1,176 @@
+"""Benchmark of the HSTU attention forward on one MI355X.
+
+A step is one call of the forward operator over the whole workload (every
+sequence and head): the mask, the non-linearity and both products run inside
+the timed kernels; inputs are resident in HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--schedule S]
+
+Prints one JSON line: effective TFLOP/s counting 2 * (hdim_qk + hdim_v) FLOPs
+per visible (b, h, i, j) pair, the roofline of the dominant kernel, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, os.path.join(ROOT, "tests")):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+METRIC = "HSTU fwd effective TFLOP/s (visible pairs) and % of bf16 MFMA peak, 1 GPU"
+DEFAULT_WORKLOAD = "jagged_silu_bf16_d128_causal_long"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "recsys_attention_amd", "csrc", f)
+                  for f in ("hstu_fwd_kernels.hip", "hstu_plan.h", "hstu_params.h")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--schedule", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (0 disables cpu_baseline)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device copy of this size (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def copy_probe(mib: int):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle, untuned, on whole sequences of the workload (all heads) until
+    about budget_s of wall time; returns TFLOP/s over the visible pairs done."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    lib = oracle.load()
+    done_pairs, secs, seqs = 0, 0.0, 0
+    order = list(range(w.batch))
+    for b in order:
+        sub = W.build("sample", dtype=w.dtype, batch=1, nhead=w.nhead, hdim_qk=w.hdim_qk,
+                      hdim_v=w.hdim_v, jagged=True, cross=w.cross, causal=w.causal,
+                      softmax=w.softmax, alpha=w.alpha, groups=[w.groups[0]] if len(w.groups) == 1
+                      else [w.groups[b // (w.batch // len(w.groups))]],
+                      uih_q=[w.uih_q[b]], targets=[w.targets[b]], uih_kv=[w.uih_kv[b]],
+                      materialize=False)
+        q0, q1 = w.q_offsets[b], w.q_offsets[b + 1]
+        k0, k1 = w.kv_offsets[b], w.kv_offsets[b + 1]
+        p = oracle.problem_of(sub)
+        if len(w.groups) == 1 and w.groups[0].attn_scale == 0.0:
+            # keep the whole workload's default scale (it does not change the work)
+            p.ga = np.array([1.0 / max(w.uih_q)], np.float64)
+        t0 = time.perf_counter()
+        _, _, pairs = oracle.forward(p, w.q[q0:q1], w.k[k0:k1], w.v[k0:k1], lib=lib)
+        secs += time.perf_counter() - t0
+        done_pairs += pairs
+        seqs += 1
+        if secs >= budget_s:
+            break
+    flops = done_pairs * 2.0 * (w.hdim_qk + w.hdim_v)
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib),
+            "kind": "oracle",
+            "sample": f"first {seqs} of {w.batch} sequences, all {w.nhead} heads "
+                      f"({done_pairs} visible pairs, {secs:.1f} s, fp64 C loops)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this operator's multi-GPU sharding is described, not built.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+    import torch
+
+    import workloads as W
+    from hip_runner import DeviceInputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = W.config(args.workload)
+    splits = args.splits or w.num_splits
+    print(f"bench: {w.name}, {w.total_q} q tokens, splits={splits}", file=sys.stderr, flush=True)
+    dev = DeviceInputs(w)
+    stream = torch.cuda.current_stream()
+    pairs = dev.count_pairs(schedule=args.schedule)
+    flops = pairs * 2.0 * (w.hdim_qk + w.hdim_v)
+
+    def step():
+        return dev.forward(num_splits=splits, schedule=args.schedule)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("kernel_hash") == kernel_hash():
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "nhead": w.nhead,
+                   "hdim_qk": w.hdim_qk, "hdim_v": w.hdim_v, "total_tokens": w.total_q,
+                   "max_seqlen": w.max_seqlen_q, "visible_pairs": pairs,
+                   "splits": splits, "schedule": args.schedule,
+                   "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+        "wall_s_timed": round(wall, 3),
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -66,6 +66,8 @@ def load(path: Optional[str] = None):
                                                 _i32p, _f64p, _f64p, ctypes.c_int]
     lib.oracle_count_pairs.argtypes = _PROBLEM + [_i64p]
     lib.oracle_seq_info.argtypes = _PROBLEM + [_i32p, _f64p]
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     for f in ("oracle_mask", "oracle_hstu_fwd", "oracle_hstu_rows", "oracle_count_pairs",
               "oracle_seq_info"):
         getattr(lib, f).restype = ctypes.c_int
@@ -174,6 +176,11 @@ def count_pairs(p: Problem, lib=None) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_count_pairs rejected its arguments")
     return out
+
+
+def num_threads(lib=None) -> int:
+    """OpenMP threads the oracle's parallel loops use by default."""
+    return int((lib or load()).oracle_num_threads())
 
 
 def seq_info(p: Problem, lib=None):

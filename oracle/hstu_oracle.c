@@ -328,6 +328,16 @@ int oracle_count_pairs(PROBLEM_ARGS, int64_t *per_seq)
     return 0;
 }
 
+/* Threads an OpenMP region of the oracle uses by default. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* The resolved per-sequence scalars, for inspection by the tests. */
 int oracle_seq_info(PROBLEM_ARGS, int32_t *info /* [B][6]: Cq Uq Tq Ck Ukv Tk */,
                     double *scale /* [B] */)

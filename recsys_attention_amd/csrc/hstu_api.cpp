@@ -1,0 +1,242 @@
+// hstu_api.cpp - the C ABI of include/hstu.h: argument validation, default
+// resolution (CK example README argument table: alpha = 0 -> 1/sqrt(hdim_qk),
+// attn_scale = 0 -> 1/max_seqlen of Q's UIH), workspace sizing and dispatch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "hstu.h"
+#include "hstu_launch.h"
+#include "hstu_plan.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+hstu_status_t fail(hstu_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t rows_q(const hstu_fwd_args_t *a) {
+    return a->jagged ? (int64_t)a->total_q : (int64_t)a->batch * a->seqlen_q;
+}
+
+hstu_status_t validate(const hstu_fwd_args_t *a) {
+    g_last_error[0] = '\0';
+    if (!a) return fail(HSTU_ERR_INVALID_ARG, "args is NULL");
+    if (a->dtype != HSTU_FP16 && a->dtype != HSTU_BF16)
+        return fail(HSTU_ERR_INVALID_ARG, "dtype %d is neither HSTU_FP16 nor HSTU_BF16", a->dtype);
+    if (a->batch < 0) return fail(HSTU_ERR_INVALID_ARG, "batch %d < 0", a->batch);
+    if (a->nhead < 1) return fail(HSTU_ERR_INVALID_ARG, "nhead %d < 1", a->nhead);
+    if (a->hdim_qk <= 0 || a->hdim_v <= 0)
+        return fail(HSTU_ERR_INVALID_ARG, "head dims must be positive (%d, %d)", a->hdim_qk, a->hdim_v);
+    if (a->hdim_qk != a->hdim_v || (a->hdim_qk != 64 && a->hdim_qk != 128 && a->hdim_qk != 256))
+        return fail(HSTU_ERR_UNSUPPORTED, "head dims (%d, %d): built for 64/64, 128/128, 256/256",
+                    a->hdim_qk, a->hdim_v);
+    for (int32_t f : {a->jagged, a->cross, a->causal, a->softmax})
+        if (f != 0 && f != 1) return fail(HSTU_ERR_INVALID_ARG, "jagged/cross/causal/softmax must be 0 or 1");
+    if (a->schedule < 0 || a->schedule > 2)
+        return fail(HSTU_ERR_INVALID_ARG, "schedule %d not in 0..2", a->schedule);
+    if (a->seqlen_q < 0 || a->seqlen_kv < 0)
+        return fail(HSTU_ERR_INVALID_ARG, "negative seqlen (%d, %d)", a->seqlen_q, a->seqlen_kv);
+    if (!a->jagged && !a->cross && a->seqlen_kv != a->seqlen_q)
+        return fail(HSTU_ERR_INVALID_ARG, "batched self-attention needs seqlen_kv == seqlen_q (%d != %d)",
+                    a->seqlen_kv, a->seqlen_q);
+    if (a->jagged) {
+        if (a->batch > 0 && !a->seq_offsets_q)
+            return fail(HSTU_ERR_INVALID_ARG, "jagged mode needs seq_offsets_q");
+        if (a->cross && a->batch > 0 && !a->seq_offsets_kv)
+            return fail(HSTU_ERR_INVALID_ARG, "jagged cross-attention needs seq_offsets_kv");
+        if (!a->cross && a->seq_offsets_kv)
+            return fail(HSTU_ERR_INVALID_ARG, "seq_offsets_kv is for cross-attention only");
+        if (a->total_q < 0) return fail(HSTU_ERR_INVALID_ARG, "total_q %d < 0", a->total_q);
+    } else if (a->seq_offsets_q || a->seq_offsets_kv) {
+        return fail(HSTU_ERR_INVALID_ARG, "seq_offsets are for jagged mode only");
+    }
+    if ((int64_t)a->batch * a->seqlen_q > INT32_MAX || (int64_t)a->batch * a->seqlen_kv > INT32_MAX)
+        return fail(HSTU_ERR_INVALID_ARG, "token count exceeds int32");
+    const bool work = rows_q(a) > 0 && a->batch > 0;
+    if (work && (!a->q || !a->k || !a->v || !a->o))
+        return fail(HSTU_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+    if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+        return fail(HSTU_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    const int64_t min_qk = (int64_t)a->nhead * a->hdim_qk, min_v = (int64_t)a->nhead * a->hdim_v;
+    const int64_t strides[4] = {a->q_tok_stride, a->k_tok_stride, a->v_tok_stride, a->o_tok_stride};
+    const int64_t mins[4] = {min_qk, min_qk, min_v, min_v};
+    for (int i = 0; i < 4; ++i) {
+        if (strides[i] == 0) continue;
+        if (strides[i] < mins[i] || strides[i] % 8 != 0)
+            return fail(HSTU_ERR_INVALID_ARG,
+                        "token stride %lld must be 0 or a multiple of 8 that is >= nhead * hdim (%lld)",
+                        (long long)strides[i], (long long)mins[i]);
+    }
+    if (a->num_groups < 1 || a->num_groups > HSTU_MAX_GROUPS)
+        return fail(HSTU_ERR_INVALID_ARG, "num_groups %d not in 1..%d", a->num_groups, HSTU_MAX_GROUPS);
+    if (a->batch % a->num_groups != 0)
+        return fail(HSTU_ERR_INVALID_ARG, "batch %d is not a multiple of num_groups %d", a->batch,
+                    a->num_groups);
+    if (!a->groups) return fail(HSTU_ERR_INVALID_ARG, "groups is NULL");
+    for (int g = 0; g < a->num_groups; ++g) {
+        const hstu_mask_group_t &m = a->groups[g];
+        if (m.local_len < 0 || m.context_len < 0 || m.minfull_len < 0)
+            return fail(HSTU_ERR_INVALID_ARG, "group %d: negative local/context/minfull length", g);
+        if (!isfinite(m.attn_scale)) return fail(HSTU_ERR_INVALID_ARG, "group %d: attn_scale not finite", g);
+        if (m.attn_scale == 0.0f && m.max_uih_q < 0)
+            return fail(HSTU_ERR_INVALID_ARG, "group %d: attn_scale 0 needs max_uih_q >= 0", g);
+    }
+    if (!isfinite(a->alpha)) return fail(HSTU_ERR_INVALID_ARG, "alpha not finite");
+    if (a->lse && !a->softmax) return fail(HSTU_ERR_INVALID_ARG, "lse output is for the softmax variant");
+    if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(HSTU_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    return HSTU_OK;
+}
+
+void fill_params(const hstu_fwd_args_t *a, int32_t num_splits, hstu::KernelParams &p) {
+    memset(&p, 0, sizeof(p));
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.o = a->o;
+    p.lse = a->lse;
+    p.q_stride = a->q_tok_stride ? a->q_tok_stride : (int64_t)a->nhead * a->hdim_qk;
+    p.k_stride = a->k_tok_stride ? a->k_tok_stride : (int64_t)a->nhead * a->hdim_qk;
+    p.v_stride = a->v_tok_stride ? a->v_tok_stride : (int64_t)a->nhead * a->hdim_v;
+    p.o_stride = a->o_tok_stride ? a->o_tok_stride : (int64_t)a->nhead * a->hdim_v;
+    p.off_q = a->seq_offsets_q;
+    p.off_kv = a->seq_offsets_kv;
+    p.num_targets = a->num_targets;
+    p.B = a->batch;
+    p.H = a->nhead;
+    p.seqlen_q = a->seqlen_q;
+    p.seqlen_kv = a->cross ? a->seqlen_kv : a->seqlen_q;
+    p.jagged = a->jagged;
+    p.cross = a->cross;
+    p.causal = a->causal;
+    p.total_rows = (int32_t)rows_q(a);
+    p.num_qt = (a->seqlen_q + hstu::kBlockM - 1) / hstu::kBlockM;
+    const int64_t bh = (int64_t)a->batch * a->nhead;
+    p.bh_pad = (int32_t)((bh + 7) / 8 * 8);
+    p.num_splits = num_splits;
+    p.schedule = a->schedule == 0 ? 1 : a->schedule;
+    p.alpha = a->alpha != 0.0f ? a->alpha : (float)(1.0 / sqrt((double)a->hdim_qk));
+    p.G = a->num_groups;
+    p.per_group = a->batch > 0 ? a->batch / a->num_groups : 1;
+    for (int g = 0; g < a->num_groups; ++g) {
+        const hstu_mask_group_t &m = a->groups[g];
+        p.groups[g].local_len = m.local_len;
+        p.groups[g].context_len = m.context_len;
+        p.groups[g].minfull_len = m.minfull_len;
+        p.groups[g].attn_scale =
+            m.attn_scale != 0.0f ? m.attn_scale
+                                 : (float)(1.0 / (double)(m.max_uih_q > 0 ? m.max_uih_q : 1));
+    }
+}
+
+size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+    if (num_splits <= 1) return 0;
+    const size_t rows = (size_t)rows_q(a) * (size_t)a->nhead * (size_t)num_splits;
+    const size_t o_bytes = rows * (size_t)a->hdim_v * sizeof(float);
+    const size_t lse_bytes = a->softmax ? rows * sizeof(float) : 0;
+    return ((o_bytes + 255) / 256) * 256 + lse_bytes;
+}
+
+hstu_status_t check_grid(const hstu::KernelParams &p) {
+    if (hstu::grid_size(p) > (int64_t)INT32_MAX)
+        return fail(HSTU_ERR_INVALID_ARG, "problem too large for one launch");
+    return HSTU_OK;
+}
+
+hstu_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return HSTU_OK;
+    return fail(HSTU_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_validate_args(const hstu_fwd_args_t *args) { return validate(args); }
+
+size_t hstu_fwd_workspace_size(const hstu_fwd_args_t *args, int32_t num_splits) {
+    if (validate(args) != HSTU_OK || num_splits < 1 || num_splits > HSTU_MAX_SPLITS) return 0;
+    return workspace_bytes(args, num_splits);
+}
+
+hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, void *hip_stream) {
+    (void)ws;
+    (void)ws_bytes;
+    hstu_status_t st = validate(args);
+    if (st != HSTU_OK) return st;
+    hstu::KernelParams p;
+    fill_params(args, 1, p);
+    if ((st = check_grid(p)) != HSTU_OK) return st;
+    if (p.total_rows == 0 || p.B == 0) return HSTU_OK;
+    return hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->softmax != 0, false,
+                                           (hipStream_t)hip_stream),
+                      "forward kernel launch");
+}
+
+hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, void *ws,
+                               size_t ws_bytes, void *hip_stream) {
+    hstu_status_t st = validate(args);
+    if (st != HSTU_OK) return st;
+    if (num_splits < 1 || num_splits > HSTU_MAX_SPLITS)
+        return fail(HSTU_ERR_INVALID_ARG, "num_splits %d not in 1..%d", num_splits, HSTU_MAX_SPLITS);
+    if (num_splits == 1) return hstu_fwd(args, ws, ws_bytes, hip_stream);
+    const size_t need = workspace_bytes(args, num_splits);
+    if (!ws || ws_bytes < need)
+        return fail(HSTU_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(HSTU_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    hstu::KernelParams p;
+    fill_params(args, num_splits, p);
+    if ((st = check_grid(p)) != HSTU_OK) return st;
+    if (p.total_rows == 0 || p.B == 0) return HSTU_OK;
+    const size_t rows = (size_t)p.total_rows * (size_t)p.H * (size_t)num_splits;
+    p.part_o = (float *)ws;
+    p.part_lse = args->softmax ? (float *)((char *)ws + ((rows * args->hdim_v * sizeof(float) + 255) / 256) * 256)
+                               : nullptr;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    st = hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->softmax != 0, true, stream),
+                    "split-KV kernel launch");
+    if (st != HSTU_OK) return st;
+    return hip_status(hstu::launch_combine(p, args->dtype, args->hdim_v, args->softmax != 0, stream),
+                      "combine kernel launch");
+}
+
+hstu_status_t hstu_count_visible_pairs(const hstu_fwd_args_t *args, unsigned long long *d_count,
+                                       void *hip_stream) {
+    hstu_status_t st = validate(args);
+    if (st != HSTU_OK) return st;
+    if (!d_count) return fail(HSTU_ERR_INVALID_ARG, "d_count is NULL");
+    hstu::KernelParams p;
+    fill_params(args, 1, p);
+    if ((st = check_grid(p)) != HSTU_OK) return st;
+    if (p.B == 0) p.num_qt = 0;
+    return hip_status(hstu::launch_count(p, args->hdim_qk, d_count, (hipStream_t)hip_stream),
+                      "count kernel launch");
+}
+
+const char *hstu_status_string(hstu_status_t s) {
+    switch (s) {
+        case HSTU_OK: return "HSTU_OK";
+        case HSTU_ERR_INVALID_ARG: return "HSTU_ERR_INVALID_ARG";
+        case HSTU_ERR_UNSUPPORTED: return "HSTU_ERR_UNSUPPORTED";
+        case HSTU_ERR_WORKSPACE: return "HSTU_ERR_WORKSPACE";
+        case HSTU_ERR_HIP: return "HSTU_ERR_HIP";
+    }
+    return "HSTU_ERR_UNKNOWN";
+}
+
+const char *hstu_last_error(void) { return g_last_error; }
+
+int32_t hstu_abi_version(void) { return HSTU_ABI_VERSION; }
+
+}  // extern "C"

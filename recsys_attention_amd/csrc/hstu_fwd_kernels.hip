@@ -1,0 +1,534 @@
+// hstu_fwd_kernels.hip - gfx950 kernels of the HSTU attention forward.
+//
+// Operator: CK example README "18_hstu_attention", "Forward computation"
+// (s = alpha * q.k, functional mask, SiLU * attn_scale or attn_scale * softmax,
+// o = p @ v) and "Split-KV" (key axis cut across work-groups + combine pass).
+//
+// Work-group = 256 threads = 4 waves; it owns BM = 128 query rows of one
+// (sequence, head), 32 rows per wave.  Within a wave, lane l owns query row
+// l % 32 and half of each key block (lane group g = l / 32):
+//   S^T = K . Q^T   v_mfma_f32_32x32x16_{bf16,f16}: A = K tile from LDS
+//                   (row = key, 8 consecutive d per lane), B = Q^T kept in
+//                   VGPRs for the whole work-group lifetime.
+//   The accumulator gives lane l the scores of its own query against 16 keys
+//   of each 32-key block, so the mask is a per-lane interval test against the
+//   row's visible key set [0, ctx) U [lo, hi].
+//   O^T += V^T . P^T   A = V^T from LDS (V is transposed while staged), B = P^T
+//                   straight from the score registers: the key order inside
+//                   each 16-key MFMA step is permuted identically on both
+//                   operands, so no cross-lane shuffle is needed.
+// K and V tiles are double-buffered in LDS; the next tile's global loads are
+// issued before the current tile's MFMAs, one barrier per tile.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "hstu_launch.h"
+#include "hstu_plan.h"
+
+namespace hstu {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<HSTU_BF16> {
+    static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+        bf16x2_t v = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+template <>
+struct Elem<HSTU_FP16> {
+    static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+        f16x2_t v = {(_Float16)x, (_Float16)y};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+// Tile geometry for head dim D (= hdim_qk = hdim_v) and key-tile width BN.
+template <int D, int BN>
+struct Tile {
+    static constexpr int BM = 128;           // query rows per work-group
+    static constexpr int NT = 256;           // threads
+    static constexpr int KS = D + 8;         // K tile row stride in LDS (elements)
+    static constexpr int VS = BN + 4;        // V^T tile row stride in LDS (elements)
+    static constexpr int KTILE = BN * KS;
+    static constexpr int VTILE = D * VS;
+    static constexpr int KSTEPS = D / 16;    // MFMA k-steps of Q.K^T
+    static constexpr int NKB = BN / 32;      // 32-key blocks per tile
+    static constexpr int NDB = D / 32;       // 32-column blocks of the output
+    static constexpr int NDVC = D / 8;       // 16-byte chunks per row
+    static constexpr int K_PER_T = BN * NDVC / NT;  // K chunks staged per thread
+    static_assert(BN * D == 8192, "every thread stages one 4x8 V block and four K chunks");
+    static_assert((BN / 4) * NDVC == NT, "V staging covers the tile exactly");
+    static_assert(K_PER_T * NT == BN * NDVC, "K staging covers the tile exactly");
+};
+
+__device__ __forceinline__ int32_t wave_min(int32_t x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = imin(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ int32_t wave_max(int32_t x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = imax(x, __shfl_xor(x, o));
+    return x;
+}
+
+// Per-work-group set-up shared by the attention and the pair-count kernels:
+// the work item, its sequence, the lane's row interval and the key-tile list.
+struct BlockPlan {
+    WorkItem it;
+    SeqGeom s;
+    RowSpan span;
+    TileList tiles;
+    int32_t row;  // row inside the sequence owned by this lane
+};
+
+template <int BN>
+__device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, BlockPlan &bp,
+                                           int32_t *red) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    bp.it = decode_work(p, blockIdx.x);
+    if (!bp.it.valid) return false;
+    bp.s = seq_geom(p, bp.it.b);
+    const int32_t r0 = bp.it.qt * 128;
+    if (r0 >= bp.s.S_q) return false;
+    bp.row = r0 + wave * 32 + (lane & 31);
+    bp.span = row_span(bp.s, p.causal, bp.row);
+    // union of the band parts over the 128 rows
+    int32_t lo = wave_min(bp.span.lo);
+    int32_t hi = wave_max(bp.span.hi);
+    if (lane == 0) {
+        red[2 * wave] = lo;
+        red[2 * wave + 1] = hi;
+    }
+    __syncthreads();
+    lo = imin(imin(red[0], red[2]), imin(red[4], red[6]));
+    hi = imax(imax(red[1], red[3]), imax(red[5], red[7]));
+    int32_t tb = 0, te = (bp.s.S_kv + BN - 1) / BN;
+    if (split) split_range(bp.s.S_kv, BN, p.num_splits, bp.it.sp, &tb, &te);
+    // rows r0.. exist (r0 < S_q), so the context tiles are needed
+    bp.tiles = make_tile_list(bp.s.Ck, true, lo, hi, BN, tb, te);
+    return true;
+}
+
+template <int DT, int D, bool SOFTMAX, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
+    constexpr int BN = key_tile_for(D);
+    using C = Tile<D, BN>;
+    using E = Elem<DT>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][C::KTILE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][C::VTILE];
+    __shared__ int32_t red[8];
+
+    BlockPlan bp;
+    if (!plan_block<BN>(p, SPLIT, bp, red)) return;
+    const SeqGeom &s = bp.s;
+    const RowSpan &span = bp.span;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+    const int h = bp.it.h;
+    const int ntiles = bp.tiles.count();
+
+    // ---- Q^T operand: lane holds d = 16*kk + 8*g .. +7 of its row
+    u32x4_t qreg[C::KSTEPS];
+    {
+        const uint16_t *qp = (const uint16_t *)p.q + (s.q0 + bp.row) * p.q_stride + h * D + g * 8;
+#pragma unroll
+        for (int kk = 0; kk < C::KSTEPS; ++kk)
+            qreg[kk] = span.valid ? *(const u32x4_t *)(qp + kk * 16) : u32x4_t{0, 0, 0, 0};
+    }
+
+    // ---- staging assignment of this thread
+    // V: a 4-key x 8-column block; within each 16 lanes (dvc_lo, kg_lo) are
+    // distinct so the transposed LDS writes spread over the banks.
+    const int v_dvc = ((tid >> 4) % (C::NDVC / 4)) * 4 + (tid & 3);
+    const int v_kg = ((tid >> 4) / (C::NDVC / 4)) * 4 + ((tid >> 2) & 3);
+    const uint16_t *kbase = (const uint16_t *)p.k + s.kv0 * p.k_stride + h * D;
+    const uint16_t *vbase = (const uint16_t *)p.v + s.kv0 * p.v_stride + h * D;
+    u32x4_t kst[C::K_PER_T];
+    u32x4_t vst[4];
+
+    auto gload = [&](int t) {
+        const int j0 = t * BN;
+#pragma unroll
+        for (int c = 0; c < C::K_PER_T; ++c) {
+            const int idx = c * C::NT + tid;
+            const int j = j0 + idx / C::NDVC;
+            kst[c] = j < s.S_kv ? *(const u32x4_t *)(kbase + (int64_t)j * p.k_stride + (idx % C::NDVC) * 8)
+                                : u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + v_kg * 4 + r;
+            vst[r] = j < s.S_kv ? *(const u32x4_t *)(vbase + (int64_t)j * p.v_stride + v_dvc * 8)
+                                : u32x4_t{0, 0, 0, 0};
+        }
+    };
+    auto stage = [&](int b) {
+#pragma unroll
+        for (int c = 0; c < C::K_PER_T; ++c) {
+            const int idx = c * C::NT + tid;
+            *(u32x4_t *)&lds_k[b][(idx / C::NDVC) * C::KS + (idx % C::NDVC) * 8] = kst[c];
+        }
+        // transpose the 4x8 block: column e of the 4 keys becomes 8 contiguous bytes
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+            for (int odd = 0; odd < 2; ++odd) {
+                const uint32_t sel = odd ? 0x07060302u : 0x05040100u;
+                u32x2_t col;
+                col.x = __builtin_amdgcn_perm(vst[1][w], vst[0][w], sel);
+                col.y = __builtin_amdgcn_perm(vst[3][w], vst[2][w], sel);
+                *(u32x2_t *)&lds_v[b][(v_dvc * 8 + 2 * w + odd) * C::VS + v_kg * 4] = col;
+            }
+        }
+    };
+
+    f32x16_t oacc[C::NDB];
+#pragma unroll
+    for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] = f32x16_t{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sc_silu = -p.alpha * kLog2e;
+    const float sc_soft = p.alpha * kLog2e;
+
+    int buf = 0;
+    if (ntiles > 0) {
+        gload(bp.tiles.at(0));
+        stage(0);
+    }
+    __syncthreads();
+
+    for (int n = 0; n < ntiles; ++n) {
+        const int t = bp.tiles.at(n);
+        const bool has_next = n + 1 < ntiles;
+        if (has_next) gload(bp.tiles.at(n + 1));
+        const int j0 = t * BN;
+        const int32_t st = tile_state(span, j0, j0 + BN);
+        const bool wave_any = __ballot(st != kTileEmpty) != 0;
+        const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
+
+        if (wave_any) {
+            // ---- S^T = K Q^T
+            f32x16_t sacc[C::NKB];
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                sacc[kb] = f32x16_t{};
+                const uint16_t *kp = &lds_k[buf][(kb * 32 + r32) * C::KS + g * 8];
+#pragma unroll
+                for (int kk = 0; kk < C::KSTEPS; ++kk)
+                    sacc[kb] = E::mfma(*(const u32x4_t *)(kp + kk * 16), qreg[kk], sacc[kb]);
+            }
+
+            // ---- mask + non-linearity; element i of block kb is key
+            //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
+            u32x4_t pb[C::NKB][2];
+            if constexpr (!SOFTMAX) {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float x = sacc[kb][i];
+                        // SiLU(alpha x) = alpha x / (1 + 2^(-alpha log2e x))
+                        float pv = (x * p.alpha) *
+                                   __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * sc_silu));
+                        if (wave_mask) {
+                            const int key = j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                            pv = span_visible(span, key) ? pv : 0.0f;
+                        }
+                        sacc[kb][i] = pv;
+                    }
+                }
+            } else {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float x = sacc[kb][i] * sc_soft;
+                        if (wave_mask) {
+                            const int key = j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                            x = span_visible(span, key) ? x : -INFINITY;
+                        }
+                        sacc[kb][i] = x;
+                        mx = fmaxf(mx, x);
+                    }
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run, mx);
+                const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+                const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+                if (__ballot(corr != 1.0f) != 0) {
+                    l_run *= corr;
+#pragma unroll
+                    for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] *= corr;
+                }
+                m_run = m_new;
+                float lsum = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float e = __builtin_amdgcn_exp2f(sacc[kb][i] - m_use);
+                        lsum += e;
+                        sacc[kb][i] = e;
+                    }
+                }
+                l_run += lsum;
+            }
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const int i0 = 8 * t2;
+                    pb[kb][t2] = u32x4_t{E::pack2(sacc[kb][i0 + 0], sacc[kb][i0 + 1]),
+                                         E::pack2(sacc[kb][i0 + 2], sacc[kb][i0 + 3]),
+                                         E::pack2(sacc[kb][i0 + 4], sacc[kb][i0 + 5]),
+                                         E::pack2(sacc[kb][i0 + 6], sacc[kb][i0 + 7])};
+                }
+            }
+
+            // ---- O^T += V^T P^T; MFMA step (kb, t2) covers keys
+            //      32kb + 16t2 + {4g..4g+3, 8+4g..8+4g+3} in both operands
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+                    for (int nb = 0; nb < C::NDB; ++nb) {
+                        const uint16_t *vp = &lds_v[buf][(nb * 32 + r32) * C::VS + kb * 32 + 16 * t2 + 4 * g];
+                        const u32x2_t a0 = *(const u32x2_t *)vp;
+                        const u32x2_t a1 = *(const u32x2_t *)(vp + 8);
+                        oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb[kb][t2], oacc[nb]);
+                    }
+                }
+            }
+        }
+
+        if (has_next) stage(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
+    float scale = s.attn_scale;
+    float lse_val = 0.f;
+    if constexpr (SOFTMAX) {
+        const float l = l_run + __shfl_xor(l_run, 32);
+        scale = l > 0.f ? s.attn_scale / l : 0.f;
+        lse_val = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    }
+    if (!span.valid) return;
+    const int64_t grow = s.q0 + bp.row;  // token row of o
+    if constexpr (!SPLIT) {
+        uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * D + 4 * g;
+#pragma unroll
+        for (int nb = 0; nb < C::NDB; ++nb) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x16_t &a = oacc[nb];
+                *(u32x2_t *)(op + nb * 32 + 8 * i4) =
+                    u32x2_t{E::pack2(a[4 * i4] * scale, a[4 * i4 + 1] * scale),
+                            E::pack2(a[4 * i4 + 2] * scale, a[4 * i4 + 3] * scale)};
+            }
+        }
+        if constexpr (SOFTMAX) {
+            if (p.lse != nullptr && g == 0) {
+                const int64_t li = p.jagged ? (int64_t)h * p.total_rows + grow
+                                            : ((int64_t)bp.it.b * p.H + h) * p.seqlen_q + bp.row;
+                p.lse[li] = lse_val;
+            }
+        }
+    } else {
+        // fp32 partials, already multiplied by attn_scale (softmax: normalised
+        // by this split's own sum; the combine pass reweights by the LSEs)
+        const int64_t prow = ((int64_t)bp.it.sp * p.total_rows + grow) * p.H + h;
+        float *pp = p.part_o + prow * D + 4 * g;
+#pragma unroll
+        for (int nb = 0; nb < C::NDB; ++nb) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x16_t &a = oacc[nb];
+                *(f32x4_t *)(pp + nb * 32 + 8 * i4) =
+                    f32x4_t{a[4 * i4] * scale, a[4 * i4 + 1] * scale, a[4 * i4 + 2] * scale,
+                            a[4 * i4 + 3] * scale};
+            }
+        }
+        if constexpr (SOFTMAX) {
+            if (g == 0) p.part_lse[prow] = lse_val;
+        }
+    }
+}
+
+// Split-KV combine: one thread per (row, head, 4 columns).
+//   SiLU:    o = sum_c o_c
+//   softmax: lse = ln sum_c exp(lse_c); o = sum_c exp(lse_c - lse) o_c
+//            (a row no split sees: o = 0, lse = -inf)
+template <int DT, bool SOFTMAX>
+__global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D) {
+    using E = Elem<DT>;
+    const int nchunk = D / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)p.total_rows * p.H * nchunk;
+    if (idx >= total) return;
+    const int chunk = (int)(idx % nchunk);
+    const int64_t rh = idx / nchunk;  // row * H + h
+    const int64_t split_stride = (int64_t)p.total_rows * p.H;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float lse = 0.f;
+    if constexpr (!SOFTMAX) {
+        for (int c = 0; c < p.num_splits; ++c)
+            acc += *(const f32x4_t *)(p.part_o + (c * split_stride + rh) * D + chunk * 4);
+    } else {
+        float mx = -INFINITY;
+        for (int c = 0; c < p.num_splits; ++c) mx = fmaxf(mx, p.part_lse[c * split_stride + rh]);
+        if (mx == -INFINITY) {
+            lse = -INFINITY;
+        } else {
+            float sum = 0.f;
+            for (int c = 0; c < p.num_splits; ++c) sum += expf(p.part_lse[c * split_stride + rh] - mx);
+            lse = mx + logf(sum);
+            for (int c = 0; c < p.num_splits; ++c) {
+                const float lc = p.part_lse[c * split_stride + rh];
+                if (lc == -INFINITY) continue;
+                acc += expf(lc - lse) * *(const f32x4_t *)(p.part_o + (c * split_stride + rh) * D + chunk * 4);
+            }
+        }
+    }
+    const int64_t grow = rh / p.H;
+    const int h = (int)(rh % p.H);
+    uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * D + chunk * 4;
+    *(u32x2_t *)op = u32x2_t{E::pack2(acc[0], acc[1]), E::pack2(acc[2], acc[3])};
+    if constexpr (SOFTMAX) {
+        if (p.lse != nullptr && chunk == 0) {
+            int64_t li;
+            if (p.jagged) {
+                li = (int64_t)h * p.total_rows + grow;
+            } else {
+                const int64_t b = grow / p.seqlen_q, i = grow % p.seqlen_q;
+                li = (b * p.H + h) * p.seqlen_q + i;
+            }
+            p.lse[li] = lse;
+        }
+    }
+}
+
+// Visible pairs inside the scheduled key tiles, counted with the forward
+// kernel's own plan and predicate (the same lane -> (row, key) assignment and
+// the same full-tile shortcut).
+template <int BN>
+__global__ __launch_bounds__(256) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
+    __shared__ int32_t red[8];
+    BlockPlan bp;
+    if (!plan_block<BN>(p, false, bp, red)) return;
+    const int lane = threadIdx.x & 63, g = lane >> 5;
+    unsigned long long mine = 0;
+    const int ntiles = bp.tiles.count();
+    for (int n = 0; n < ntiles; ++n) {
+        const int j0 = bp.tiles.at(n) * BN;
+        const int32_t st = tile_state(bp.span, j0, j0 + BN);
+        const bool wave_any = __ballot(st != kTileEmpty) != 0;
+        const bool wave_mask = __ballot(bp.span.valid && st != kTileFull) != 0;
+        if (!wave_any || !bp.span.valid) continue;
+        if (!wave_mask) {
+            mine += BN / 2;
+            continue;
+        }
+        for (int kb = 0; kb < BN / 32; ++kb)
+            for (int i = 0; i < 16; ++i)
+                mine += span_visible(bp.span, j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3)) ? 1 : 0;
+    }
+    for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o);
+    if (lane == 0 && mine) atomicAdd(count, mine);
+}
+
+__global__ void hstu_zero_u64(unsigned long long *x) { *x = 0; }
+
+// ------------------------------------------------------------------ launchers
+
+template <int DT, int D, bool SOFTMAX, bool SPLIT>
+static hipError_t launch_one(const KernelParams &p, hipStream_t stream) {
+    const int64_t grid = grid_size(p);
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+static hipError_t launch_d(const KernelParams &p, bool softmax, bool split, hipStream_t stream) {
+    if (softmax) return split ? launch_one<DT, D, true, true>(p, stream) : launch_one<DT, D, true, false>(p, stream);
+    return split ? launch_one<DT, D, false, true>(p, stream) : launch_one<DT, D, false, false>(p, stream);
+}
+
+template <int DT>
+static hipError_t launch_dt(const KernelParams &p, int D, bool softmax, bool split, hipStream_t stream) {
+    switch (D) {
+        case 64: return launch_d<DT, 64>(p, softmax, split, stream);
+        case 128: return launch_d<DT, 128>(p, softmax, split, stream);
+        case 256: return launch_d<DT, 256>(p, softmax, split, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_forward(const KernelParams &p, int dtype, int D, bool softmax, bool split,
+                          hipStream_t stream) {
+    return dtype == HSTU_BF16 ? launch_dt<HSTU_BF16>(p, D, softmax, split, stream)
+                              : launch_dt<HSTU_FP16>(p, D, softmax, split, stream);
+}
+
+hipError_t launch_combine(const KernelParams &p, int dtype, int D, bool softmax, hipStream_t stream) {
+    const int64_t total = (int64_t)p.total_rows * p.H * (D / 4);
+    if (total <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (dtype == HSTU_BF16) {
+        if (softmax)
+            hipLaunchKernelGGL((hstu_combine_kernel<HSTU_BF16, true>), dim3(blocks), dim3(256), 0, stream, p, D);
+        else
+            hipLaunchKernelGGL((hstu_combine_kernel<HSTU_BF16, false>), dim3(blocks), dim3(256), 0, stream, p, D);
+    } else {
+        if (softmax)
+            hipLaunchKernelGGL((hstu_combine_kernel<HSTU_FP16, true>), dim3(blocks), dim3(256), 0, stream, p, D);
+        else
+            hipLaunchKernelGGL((hstu_combine_kernel<HSTU_FP16, false>), dim3(blocks), dim3(256), 0, stream, p, D);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_count(const KernelParams &p, int D, unsigned long long *count, hipStream_t stream) {
+    hipLaunchKernelGGL(hstu_zero_u64, dim3(1), dim3(1), 0, stream, count);
+    const int64_t grid = grid_size(p);
+    if (grid > 0) {
+        switch (D) {
+            case 64: hipLaunchKernelGGL(hstu_count_kernel<key_tile_for(64)>, dim3((unsigned)grid), dim3(256), 0, stream, p, count); break;
+            case 128: hipLaunchKernelGGL(hstu_count_kernel<key_tile_for(128)>, dim3((unsigned)grid), dim3(256), 0, stream, p, count); break;
+            case 256: hipLaunchKernelGGL(hstu_count_kernel<key_tile_for(256)>, dim3((unsigned)grid), dim3(256), 0, stream, p, count); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hstu

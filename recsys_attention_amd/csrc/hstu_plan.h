@@ -1,0 +1,212 @@
+// hstu_plan.h - per-sequence geometry, per-row visible key intervals, key-tile
+// classification and work decoding of the HSTU forward kernels.
+//
+// The functional mask (CK example README "18_hstu_attention", "Masking" table) is
+// evaluated here in interval form: every query row i of a sequence sees the keys
+//     [0, ctx)  U  [lo, hi]          (physical key indices; lo > hi: empty)
+// where [0, ctx) is the context prefix (visible to all queries) and [lo, hi] the
+// band of UIH keys its causal / local-window / min-full components leave visible.
+// Target keys lie beyond every hi, so they are never attended.  Nothing here
+// depends on HIP; host and device code include it.
+#pragma once
+
+#include <stdint.h>
+
+#include "hstu_params.h"
+
+#if defined(__HIPCC__)
+#define HSTU_HD __host__ __device__ __forceinline__
+#else
+#define HSTU_HD inline
+#endif
+
+namespace hstu {
+
+constexpr int32_t kEmptyLo = 0x3fffffff;
+constexpr int32_t kEmptyHi = -0x3fffffff;
+
+HSTU_HD int32_t imin(int32_t a, int32_t b) { return a < b ? a : b; }
+HSTU_HD int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
+
+// Class boundaries of one sequence (README "Masking": physical lengths are
+// context + UIH + targets; cross-attention keys carry no targets).
+struct SeqGeom {
+    int64_t q0, kv0;   // first token in q/o and in k/v
+    int32_t S_q, S_kv; // physical lengths
+    int32_t Cq, Uq;    // query-side context and UIH counts (targets follow)
+    int32_t Ck, Ukv;   // key-side context and UIH counts
+    int32_t L, M;      // local_len, minfull_len
+    int32_t group;
+    float attn_scale;
+};
+
+HSTU_HD SeqGeom seq_geom(const KernelParams &p, int32_t b) {
+    SeqGeom s;
+    s.group = b / p.per_group;
+    const GroupDev &g = p.groups[s.group];
+    if (p.jagged) {
+        s.q0 = p.off_q[b];
+        s.S_q = (int32_t)(p.off_q[b + 1] - p.off_q[b]);
+        if (p.cross) {
+            s.kv0 = p.off_kv[b];
+            s.S_kv = (int32_t)(p.off_kv[b + 1] - p.off_kv[b]);
+        } else {
+            s.kv0 = s.q0;
+            s.S_kv = s.S_q;
+        }
+    } else {
+        s.q0 = (int64_t)b * p.seqlen_q;
+        s.kv0 = (int64_t)b * p.seqlen_kv;
+        s.S_q = p.seqlen_q;
+        s.S_kv = p.seqlen_kv;
+    }
+    const int32_t T = p.num_targets ? imax(p.num_targets[b], 0) : 0;
+    s.Cq = imin(g.context_len, s.S_q);
+    const int32_t Tq = imin(T, s.S_q - s.Cq);
+    s.Uq = s.S_q - s.Cq - Tq;
+    s.Ck = imin(g.context_len, s.S_kv);
+    const int32_t Tk = p.cross ? 0 : imin(T, s.S_kv - s.Ck);
+    s.Ukv = s.S_kv - s.Ck - Tk;
+    s.L = g.local_len;
+    s.M = g.minfull_len;
+    s.attn_scale = g.attn_scale;
+    return s;
+}
+
+// Visible keys of query row i: [0, ctx) U [lo, hi].  Rows outside the
+// sequence see nothing (ctx = 0, empty band).
+struct RowSpan {
+    int32_t ctx, lo, hi;
+    bool valid;
+};
+
+HSTU_HD RowSpan row_span(const SeqGeom &s, int32_t causal, int32_t i) {
+    RowSpan r;
+    r.lo = kEmptyLo;
+    r.hi = kEmptyHi;
+    r.valid = (i >= 0 && i < s.S_q);
+    if (!r.valid) {
+        r.ctx = 0;
+        return r;
+    }
+    r.ctx = s.Ck;
+    int32_t x;
+    bool full;
+    if (i < s.Cq) {                   // context query: before every UIH key
+        if (causal) return r;
+        x = -1;
+        full = (s.L == 0);
+    } else if (i < s.Cq + s.Uq) {     // UIH query at UIH position u
+        const int32_t u = i - s.Cq;
+        x = u + (s.Ukv - s.Uq);       // aligned to the tail of the key history
+        full = (s.L == 0) || (s.M > 0 && u >= s.Uq - s.M);
+    } else {                          // target query: after the whole history
+        x = s.Ukv;
+        full = (s.L == 0) || (s.M > 0);
+    }
+    const int32_t last = s.Ukv - 1;
+    const int32_t hi = causal ? imin(x, last) : (full ? last : imin(x + s.L, last));
+    const int32_t lo = full ? 0 : imax(0, x - s.L);
+    if (lo <= hi) {
+        r.lo = s.Ck + lo;
+        r.hi = s.Ck + hi;
+    }
+    return r;
+}
+
+HSTU_HD bool span_visible(const RowSpan &r, int32_t j) {
+    return j < r.ctx || (j >= r.lo && j <= r.hi);
+}
+
+// Relation of a row to the key tile [j0, j1): nothing visible, everything
+// visible, or a mix (the predicate must then be applied per key).  A row
+// outside the sequence is EMPTY.
+enum TileState : int32_t { kTileEmpty = 0, kTilePartial = 1, kTileFull = 2 };
+
+HSTU_HD int32_t tile_state(const RowSpan &r, int32_t j0, int32_t j1) {
+    if (!r.valid) return kTileEmpty;
+    const bool any = (j0 < r.ctx) || (r.lo <= r.hi && r.lo < j1 && r.hi >= j0);
+    if (!any) return kTileEmpty;
+    if (j1 <= r.ctx) return kTileFull;
+    const bool all = r.lo <= imax(j0, r.ctx) && j1 - 1 <= r.hi;
+    return all ? kTileFull : kTilePartial;
+}
+
+// Key tiles a q-tile needs: the context tiles [0, ceil(ctx/BN)) and the band
+// tiles covering [band_lo, band_hi] (the union of its rows' bands), merged when
+// they touch, then intersected with the split's tile range [t_begin, t_end).
+struct TileList {
+    int32_t a0, a1; // first range [a0, a1)
+    int32_t b0, b1; // second range [b0, b1)
+    HSTU_HD int32_t count() const { return (a1 - a0) + (b1 - b0); }
+    HSTU_HD int32_t at(int32_t n) const { return n < a1 - a0 ? a0 + n : b0 + (n - (a1 - a0)); }
+};
+
+HSTU_HD TileList make_tile_list(int32_t ctx, bool any_valid_row, int32_t band_lo, int32_t band_hi,
+                                int32_t BN, int32_t t_begin, int32_t t_end) {
+    TileList t;
+    int32_t ca = 0, cb = any_valid_row ? (ctx + BN - 1) / BN : 0;   // context tiles
+    int32_t ba = 0, bb = 0;                                            // band tiles
+    if (band_lo <= band_hi) {
+        ba = band_lo / BN;
+        bb = band_hi / BN + 1;
+    }
+    if (bb > ba && cb > ca && ba <= cb) {  // touching or overlapping: one range
+        cb = imax(cb, bb);
+        ba = bb = 0;
+    }
+    t.a0 = imax(ca, t_begin);
+    t.a1 = imin(cb, t_end);
+    if (t.a1 < t.a0) t.a1 = t.a0;
+    t.b0 = imax(ba, t_begin);
+    t.b1 = imin(bb, t_end);
+    if (t.b1 < t.b0) t.b1 = t.b0;
+    return t;
+}
+
+// Tiles [t_begin, t_end) of split sp: the sequence's key tiles cut into
+// num_splits contiguous chunks of ceil(ntiles / num_splits) tiles.
+HSTU_HD void split_range(int32_t S_kv, int32_t BN, int32_t num_splits, int32_t sp, int32_t *t_begin,
+                         int32_t *t_end) {
+    const int32_t nt = (S_kv + BN - 1) / BN;
+    const int32_t per = (nt + num_splits - 1) / num_splits;
+    *t_begin = imin(sp * per, nt);
+    *t_end = imin((sp + 1) * per, nt);
+}
+
+// Work item of a work-group: (sequence b, head h, q-tile qt, split sp).
+struct WorkItem {
+    int32_t b, h, qt, sp;
+    bool valid;
+};
+
+// Schedules (the hardware hands consecutive work-group ids to the 8 XCDs in
+// turn, so id % 8 is the XCD; both orders keep every (b, h) on one XCD):
+//  1: q-tile levels, heaviest (last) q-tile of every (b, h) first;
+//  2: per XCD, the (b, h) pairs one after another, each with all its q-tiles
+//     heaviest first, so the q-tiles reading the same keys run together.
+HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
+    WorkItem it;
+    int64_t bh, rest;
+    if (p.schedule == 2) {
+        const int64_t xcd = w % 8, loc = w / 8;
+        const int64_t per_bh = (int64_t)p.num_qt * p.num_splits;
+        bh = (loc / per_bh) * 8 + xcd;
+        rest = loc % per_bh;
+    } else {
+        bh = w % p.bh_pad;
+        rest = w / p.bh_pad;
+    }
+    it.sp = (int32_t)(rest % p.num_splits);
+    it.qt = p.num_qt - 1 - (int32_t)(rest / p.num_splits);
+    it.b = (int32_t)(bh / p.H);
+    it.h = (int32_t)(bh % p.H);
+    it.valid = bh < (int64_t)p.B * p.H && it.qt >= 0;
+    return it;
+}
+
+HSTU_HD int64_t grid_size(const KernelParams &p) {
+    return (int64_t)p.bh_pad * p.num_qt * p.num_splits;
+}
+
+}  // namespace hstu

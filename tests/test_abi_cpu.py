@@ -1,0 +1,139 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from recsys_attention_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        from recsys_attention_amd import build
+        build.build()
+    return _abi.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(hstu_[a-z_]+)\s*\(", text))
+
+
+def test_header_symbols_exported(lib):
+    declared = _declared_functions()
+    assert declared == set(_abi.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.hstu_abi_version() == _abi.HSTU_ABI_VERSION
+
+
+def _args(**over):
+    """A valid jagged bf16 hdim-128 argument block with fake (never dereferenced) pointers."""
+    groups = (_abi.MaskGroupC * 1)()
+    groups[0].local_len, groups[0].context_len, groups[0].minfull_len = 5, 6, 6
+    groups[0].attn_scale, groups[0].max_uih_q = 0.0, 870
+    a = _abi.FwdArgsC(dtype=_abi.HSTU_BF16, batch=10, nhead=4, hdim_qk=128, hdim_v=128,
+                      jagged=1, cross=0, seqlen_q=881, seqlen_kv=881, total_q=8038,
+                      q=0x10000, k=0x20000, v=0x30000, o=0x40000, seq_offsets_q=0x50000,
+                      num_targets=0x60000, causal=1, softmax=0, alpha=0.0, num_groups=1,
+                      schedule=0)
+    a.groups = ctypes.cast(groups, ctypes.POINTER(_abi.MaskGroupC))
+    a._keep = groups
+    for k, v in over.items():
+        if k == "group":
+            for gk, gv in v.items():
+                setattr(groups[0], gk, gv)
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def test_valid_args_pass(lib):
+    assert lib.hstu_validate_args(ctypes.byref(_args())) == _abi.HSTU_OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(batch=-1), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(nhead=0), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(hdim_qk=96, hdim_v=64), _abi.HSTU_ERR_UNSUPPORTED),
+    (dict(hdim_qk=32, hdim_v=32), _abi.HSTU_ERR_UNSUPPORTED),
+    (dict(seq_offsets_q=None), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(cross=1), _abi.HSTU_ERR_INVALID_ARG),            # jagged cross without kv offsets
+    (dict(q=None), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(o=0x40008), _abi.HSTU_ERR_INVALID_ARG),           # misaligned
+    (dict(q_tok_stride=100), _abi.HSTU_ERR_INVALID_ARG),    # < nhead * hdim
+    (dict(q_tok_stride=516), _abi.HSTU_ERR_INVALID_ARG),    # not a multiple of 8
+    (dict(num_groups=3), _abi.HSTU_ERR_INVALID_ARG),        # 10 % 3 != 0
+    (dict(num_groups=0), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(groups=None), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(group=dict(local_len=-1)), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(group=dict(max_uih_q=-1)), _abi.HSTU_ERR_INVALID_ARG),  # attn_scale 0 needs it
+    (dict(alpha=float("nan")), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(lse=0x70000), _abi.HSTU_ERR_INVALID_ARG),         # lse without softmax
+    (dict(causal=2), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(schedule=3), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(jagged=0, seqlen_kv=5), _abi.HSTU_ERR_INVALID_ARG),  # batched self needs equal lengths
+])
+def test_invalid_args_rejected(lib, over, status):
+    a = _args(**over)
+    assert lib.hstu_validate_args(ctypes.byref(a)) == status
+    assert lib.hstu_last_error()
+    # the compute entry points reject the same block before touching the GPU
+    assert lib.hstu_fwd(ctypes.byref(a), None, 0, None) == status
+    assert lib.hstu_count_visible_pairs(ctypes.byref(a), ctypes.c_void_p(0x80000), None) == status
+
+
+def test_null_args(lib):
+    assert lib.hstu_validate_args(None) == _abi.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_fwd(None, None, 0, None) == _abi.HSTU_ERR_INVALID_ARG
+
+
+def test_workspace_size_and_checks(lib):
+    a = _args(softmax=1)
+    assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 1) == 0
+    n = lib.hstu_fwd_workspace_size(ctypes.byref(a), 16)
+    rows = 8038 * 4 * 16
+    o_bytes = (rows * 128 * 4 + 255) // 256 * 256
+    assert n == o_bytes + rows * 4
+    assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 0) == 0
+    assert lib.hstu_fwd_workspace_size(ctypes.byref(a), _abi.HSTU_MAX_SPLITS + 1) == 0
+    # missing or short workspace is reported before any launch
+    assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, None, 0, None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, ctypes.c_void_p(0x90000), n - 1,
+                                None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_fwd_splitkv(ctypes.byref(a), 0, None, 0, None) == _abi.HSTU_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    for s, name in [(0, "HSTU_OK"), (1, "HSTU_ERR_INVALID_ARG"), (2, "HSTU_ERR_UNSUPPORTED"),
+                    (3, "HSTU_ERR_WORKSPACE"), (4, "HSTU_ERR_HIP")]:
+        assert lib.hstu_status_string(s).decode() == name
+
+
+def test_product_path_does_not_use_the_oracle():
+    """The HIP library and its binding never import, link or call the oracle."""
+    pkg = os.path.join(ROOT, "recsys_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+                assert "workloads" not in text, f
+
+
+def test_binding_raises_without_library(tmp_path):
+    saved = _abi._lib
+    _abi._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            _abi.load(str(tmp_path / "missing.so"))
+    finally:
+        _abi._lib = saved

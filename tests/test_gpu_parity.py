@@ -1,0 +1,209 @@
+"""GPU parity of the HIP HSTU forward against the CPU oracle (through the C ABI).
+
+Every case draws seeded inputs (workloads), runs the HIP library on cuda:0 and
+the oracle on the host from the same rounded bits, and compares elementwise with
+the operator's tolerance (bf16: 2e-2 + 2e-2|ref|, fp16: 1e-2 + 1e-2|ref|) plus
+scale-aware checks.  Visible-pair counts must match exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from hip_runner import DeviceInputs, compare, compare_lse, lse_tokens, o_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import recsys_attention_amd as hip
+    hip._abi.load()  # raises when the library is missing: no silent fallback
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _check_full(w, num_splits=1, schedule=0, nthreads=0, elementwise=True):
+    _log(f"case {w.name}: B={w.batch} H={w.nhead} d={w.hdim_qk} splits={num_splits} "
+         f"schedule={schedule}")
+    dev = DeviceInputs(w)
+    res = dev.forward(num_splits=num_splits, schedule=schedule)
+    torch.cuda.synchronize()
+    o, lse = (res if w.softmax else (res, None))
+    p = oracle.problem_of(w)
+    o_ref, lse_ref, pairs = oracle.forward(p, w.q, w.k, w.v, nthreads=nthreads)
+    stats = compare(o_tokens(w, o), o_ref, w.dtype, w.name, elementwise=elementwise)
+    _log(f"  max err {stats['max_err']:.3e}, max |ref| {stats['scale']:.3e}, "
+         f"worst row error / row max {stats['max_row_rel']:.2e}")
+    if w.softmax:
+        compare_lse(lse_tokens(w, lse), lse_ref, w.name)
+    assert dev.count_pairs(schedule=schedule) == pairs
+    return stats
+
+
+@pytest.mark.parametrize("name", ["batched_silu_fp16_d64", "jagged_silu_bf16_d128_local",
+                                  "group4_silu_bf16_d256"])
+def test_config_parity(name):
+    w = W.config(name)
+    _check_full(w)
+
+
+def test_config_parity_with_unit_attn_scale():
+    """The configs' attn_scale makes |o| small; rerun them with attn_scale = 1 under the
+    row-relative bound (the elementwise bound is stated for the configs' own scale)."""
+    for name in ["batched_silu_fp16_d64", "jagged_silu_bf16_d128_local", "group4_silu_bf16_d256"]:
+        w = W.config(name)
+        for g in w.groups:
+            g.attn_scale = 1.0
+        _check_full(w, elementwise=False)
+
+
+def test_cross_softmax_splitkv_config():
+    w = W.config("cross_softmax_lse_splitkv16_bf16_d128")
+    _check_full(w, num_splits=w.num_splits)
+    _check_full(w, num_splits=1)
+
+
+def test_long_causal_config_sampled_rows():
+    """The full-size jagged causal workload in the benchmark's launch configuration,
+    checked on sampled rows (the oracle evaluates them one by one) and on the exact
+    visible-pair count."""
+    w = W.config("jagged_silu_bf16_d128_causal_long")
+    _log(f"case {w.name}: full size, {w.total_q} tokens")
+    dev = DeviceInputs(w)
+    o = dev.forward()
+    torch.cuda.synchronize()
+    got = o_tokens(w, o)
+    rng = np.random.default_rng(7)
+    rows_b, rows_h, rows_i = [], [], []
+    for b in range(w.batch):
+        S = w.seqlen_q[b]
+        picks = {0, 5, 6, 127, 128, S - 1, S - 2, S - w.targets[b] - 1, S - w.targets[b]}
+        picks |= set(rng.integers(0, S, size=4).tolist())
+        for i in sorted(x for x in picks if 0 <= x < S):
+            rows_b.append(b)
+            rows_i.append(i)
+            rows_h.append(int(rng.integers(0, w.nhead)))
+    p = oracle.problem_of(w)
+    ref, _ = oracle.rows(p, w.q, w.k, w.v, rows_b, rows_h, rows_i)
+    toks = np.array([w.q_offsets[b] + i for b, i in zip(rows_b, rows_i)])
+    compare(got[toks, rows_h], ref, w.dtype, w.name)
+    assert dev.count_pairs() == int(oracle.count_pairs(p).sum()) * w.nhead
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_bf16_silu(seed):
+    rng = np.random.default_rng(100 + seed)
+    d = int(rng.choice([64, 128, 256]))
+    w = W.random_workload(seed, dtype="bf16", hdim_qk=d, jagged=bool(seed % 2 == 0),
+                          cross=bool(seed % 3 == 1), max_uih=int(rng.choice([40, 200, 400])))
+    _check_full(w, schedule=1 + seed % 2)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_small_softmax(seed):
+    rng = np.random.default_rng(200 + seed)
+    d = int(rng.choice([64, 128, 256]))
+    dt = "fp16" if seed % 2 else "bf16"
+    w = W.random_workload(50 + seed, dtype=dt, hdim_qk=d, softmax=True, jagged=bool(seed % 3),
+                          cross=bool(seed % 4 == 3), max_uih=300)
+    _check_full(w, num_splits=int(rng.choice([1, 2, 5])))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_non_causal(seed):
+    w = W.random_workload(300 + seed, causal=False, softmax=bool(seed % 2), hdim_qk=128,
+                          max_uih=150)
+    _check_full(w)
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_splitkv_matches_unsplit(softmax):
+    w = W.random_workload(11, softmax=softmax, hdim_qk=128, batch=3, nhead=2, max_uih=700,
+                          groups=[W.MaskGroup(0, 6, 0, 0.0)])
+    dev = DeviceInputs(w)
+    base = dev.forward()
+    base_o = o_tokens(w, base[0] if softmax else base)
+    for ns in (1, 2, 3, 16, 64):
+        _log(f"split {ns}")
+        r = dev.forward(num_splits=ns)
+        o = o_tokens(w, r[0] if softmax else r)
+        compare(o, base_o, w.dtype, f"splits={ns}")
+        if softmax:
+            compare_lse(lse_tokens(w, r[1]), lse_tokens(w, base[1]), f"splits={ns}")
+
+
+def test_schedules_agree_bitwise():
+    w = W.config("jagged_silu_bf16_d128_local")
+    dev = DeviceInputs(w)
+    a = dev.forward(schedule=1)
+    b = dev.forward(schedule=2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_jagged_equal_lengths_equals_batched():
+    wb = W.random_workload(21, jagged=False, batch=3, nhead=2, hdim_qk=128, max_uih=190)
+    wj = W.build("jag", dtype=wb.dtype, batch=3, nhead=2, hdim_qk=128, hdim_v=128, jagged=True,
+                 cross=False, causal=True, softmax=False, alpha=0.0, groups=wb.groups,
+                 uih_q=wb.uih_q, targets=wb.targets, materialize=False)
+    wj.q, wj.k, wj.v = wb.q, wb.k, wb.v
+    wj.q_bits, wj.k_bits, wj.v_bits = wb.q_bits, wb.k_bits, wb.v_bits
+    ob = DeviceInputs(wb).forward()
+    oj = DeviceInputs(wj).forward()
+    torch.cuda.synchronize()
+    assert torch.equal(ob.reshape(oj.shape), oj)
+
+
+def test_group_equals_separate_calls():
+    w = W.config("group4_silu_bf16_d256")
+    full = o_tokens(w, DeviceInputs(w).forward())
+    per = w.batch // len(w.groups)
+    for g in range(len(w.groups)):
+        bs = list(range(g * per, (g + 1) * per))
+        sub = W.build("sub", dtype=w.dtype, batch=per, nhead=w.nhead, hdim_qk=w.hdim_qk,
+                      hdim_v=w.hdim_v, jagged=True, cross=False, causal=True, softmax=False,
+                      alpha=w.alpha, groups=[w.groups[g]], uih_q=[w.uih_q[b] for b in bs],
+                      targets=[w.targets[b] for b in bs], materialize=False)
+        t0, t1 = w.q_offsets[bs[0]], w.q_offsets[bs[-1] + 1]
+        sub.q_bits, sub.k_bits, sub.v_bits = w.q_bits[t0:t1], w.k_bits[t0:t1], w.v_bits[t0:t1]
+        # a single group's default scale uses the group's own max, which the full
+        # call also uses, so the outputs must agree bit for bit
+        got = o_tokens(sub, DeviceInputs(sub).forward())
+        assert np.array_equal(got, full[t0:t1])
+
+
+def test_edge_cases_jagged():
+    """Empty sequences, all-target sequences, context longer than the sequence, one token."""
+    groups = [W.MaskGroup(local_len=3, context_len=4, minfull_len=2, attn_scale=0.5)]
+    for softmax in (False, True):
+        w = W.build("edges", dtype="bf16", batch=6, nhead=2, hdim_qk=64, hdim_v=64, jagged=True,
+                    cross=False, causal=True, softmax=softmax, alpha=0.0, groups=groups,
+                    uih_q=[0, 0, 1, 0, 129, 3], targets=[0, 5, 0, 1, 2, 0], seed=5)
+        # sequence 0 is only context (4 tokens); 1 has 4 context + 5 targets
+        _check_full(w)
+
+
+def test_fully_masked_rows_softmax():
+    """Cross attention with U_q > U_kv and no context: leading rows see nothing:
+    o = 0 and LSE = -inf there."""
+    groups = [W.MaskGroup(0, 0, 0, 1.0)]
+    w = W.build("masked", dtype="bf16", batch=2, nhead=2, hdim_qk=128, hdim_v=128, jagged=True,
+                cross=True, causal=True, softmax=True, alpha=0.0, groups=groups,
+                uih_q=[150, 40], targets=[0, 3], uih_kv=[20, 60], seed=9)
+    _check_full(w)
+    _check_full(w, num_splits=3)
+
+
+def test_max_head_dim_and_ragged_tiles():
+    """hdim 256 with lengths that leave ragged q and key tiles in every sequence."""
+    groups = [W.MaskGroup(0, 6, 0, 0.0)]
+    w = W.build("ragged256", dtype="bf16", batch=3, nhead=3, hdim_qk=256, hdim_v=256, jagged=True,
+                cross=False, causal=True, softmax=False, alpha=0.0, groups=groups,
+                uih_q=[1, 257, 300], targets=[31, 0, 7], seed=3)
+    _check_full(w)
