@@ -109,7 +109,7 @@ typedef struct {
     const hstu_mask_group_t *groups; /* host array [num_groups], read during the call only */
     float *lse; /* softmax only, device, NULL = not saved: batched [B][H][S_q], jagged [H][total_q];
                    natural log; -inf for a row that sees no key */
-    int32_t schedule; /* work order: 0 = default, 1 = q-tile levels heavy-first,
+    int32_t schedule; /* work order: 0 = default (2), 1 = q-tile levels heavy-first,
                          2 = per-XCD sequence groups (each (b,h) kept on one XCD's L2) */
 } hstu_fwd_args_t;
 

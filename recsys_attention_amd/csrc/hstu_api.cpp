@@ -78,6 +78,15 @@ hstu_status_t validate(const hstu_fwd_args_t *a) {
                         "token stride %lld must be 0 or a multiple of 8 that is >= nhead * hdim (%lld)",
                         (long long)strides[i], (long long)mins[i]);
     }
+    {
+        // the kernels address one (sequence, head) through 32-bit byte offsets
+        const int64_t sq = (int64_t)a->seqlen_q, skv = a->cross ? (int64_t)a->seqlen_kv : sq;
+        const int64_t qs = strides[0] ? strides[0] : mins[0], ks = strides[1] ? strides[1] : mins[1],
+                      vs = strides[2] ? strides[2] : mins[2];
+        if (sq * qs * 2 >= ((int64_t)1 << 32) || skv * ks * 2 >= ((int64_t)1 << 32) ||
+            skv * vs * 2 >= ((int64_t)1 << 32))
+            return fail(HSTU_ERR_UNSUPPORTED, "one sequence spans 4 GiB or more of q, k or v");
+    }
     if (a->num_groups < 1 || a->num_groups > HSTU_MAX_GROUPS)
         return fail(HSTU_ERR_INVALID_ARG, "num_groups %d not in 1..%d", a->num_groups, HSTU_MAX_GROUPS);
     if (a->batch % a->num_groups != 0)
@@ -124,7 +133,7 @@ void fill_params(const hstu_fwd_args_t *a, int32_t num_splits, hstu::KernelParam
     const int64_t bh = (int64_t)a->batch * a->nhead;
     p.bh_pad = (int32_t)((bh + 7) / 8 * 8);
     p.num_splits = num_splits;
-    p.schedule = a->schedule == 0 ? 1 : a->schedule;
+    p.schedule = a->schedule == 0 ? 2 : a->schedule;
     p.alpha = a->alpha != 0.0f ? a->alpha : (float)(1.0 / sqrt((double)a->hdim_qk));
     p.G = a->num_groups;
     p.per_group = a->batch > 0 ? a->batch / a->num_groups : 1;

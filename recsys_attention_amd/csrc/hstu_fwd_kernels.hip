@@ -135,6 +135,44 @@ __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, Bl
     return true;
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads past the end return 0,
+// which zero-fills the ragged tail of a sequence without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// SiLU on one 32-key block of scores, in place: p = alpha x / (1 + 2^(-alpha log2e x)),
+// zeroed outside the row's visible keys when MASK.
+template <bool MASK>
+__device__ __forceinline__ void silu_block(f32x16_t &x, float alpha, float neg_alpha_log2e,
+                                           const RowSpan &span, int key0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float v = x[i];
+        float pv = (v * alpha) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * neg_alpha_log2e));
+        if constexpr (MASK) pv = span_visible(span, key0 + 8 * (i >> 2) + (i & 3)) ? pv : 0.0f;
+        x[i] = pv;
+    }
+}
+
+// Softmax scores of one block in the log2 domain, -inf outside the visible keys.
+template <bool MASK>
+__device__ __forceinline__ float scale_block(f32x16_t &x, float sc, const RowSpan &span, int key0) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float v = x[i] * sc;
+        if constexpr (MASK) v = span_visible(span, key0 + 8 * (i >> 2) + (i & 3)) ? v : -INFINITY;
+        x[i] = v;
+        mx = fmaxf(mx, v);
+    }
+    return mx;
+}
+
 template <int DT, int D, bool SOFTMAX, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
@@ -152,40 +190,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
     const int h = bp.it.h;
     const int ntiles = bp.tiles.count();
 
+    // Buffer descriptors over this (sequence, head): rows past the sequence read as 0.
+    const uint32_t qs2 = (uint32_t)p.q_stride * 2, ks2 = (uint32_t)p.k_stride * 2,
+                   vs2 = (uint32_t)p.v_stride * 2;
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc((const uint16_t *)p.q + s.q0 * p.q_stride + h * D, (uint32_t)s.S_q * qs2);
+    const __amdgpu_buffer_rsrc_t kr =
+        make_rsrc((const uint16_t *)p.k + s.kv0 * p.k_stride + h * D, (uint32_t)s.S_kv * ks2);
+    const __amdgpu_buffer_rsrc_t vr =
+        make_rsrc((const uint16_t *)p.v + s.kv0 * p.v_stride + h * D, (uint32_t)s.S_kv * vs2);
+
     // ---- Q^T operand: lane holds d = 16*kk + 8*g .. +7 of its row
     u32x4_t qreg[C::KSTEPS];
-    {
-        const uint16_t *qp = (const uint16_t *)p.q + (s.q0 + bp.row) * p.q_stride + h * D + g * 8;
 #pragma unroll
-        for (int kk = 0; kk < C::KSTEPS; ++kk)
-            qreg[kk] = span.valid ? *(const u32x4_t *)(qp + kk * 16) : u32x4_t{0, 0, 0, 0};
-    }
+    for (int kk = 0; kk < C::KSTEPS; ++kk)
+        qreg[kk] = buf_load16(qr, (uint32_t)bp.row * qs2 + (kk * 16 + g * 8) * 2);
 
     // ---- staging assignment of this thread
     // V: a 4-key x 8-column block; within each 16 lanes (dvc_lo, kg_lo) are
     // distinct so the transposed LDS writes spread over the banks.
     const int v_dvc = ((tid >> 4) % (C::NDVC / 4)) * 4 + (tid & 3);
     const int v_kg = ((tid >> 4) / (C::NDVC / 4)) * 4 + ((tid >> 2) & 3);
-    const uint16_t *kbase = (const uint16_t *)p.k + s.kv0 * p.k_stride + h * D;
-    const uint16_t *vbase = (const uint16_t *)p.v + s.kv0 * p.v_stride + h * D;
     u32x4_t kst[C::K_PER_T];
     u32x4_t vst[4];
 
+    // loads of key tile t (rows past the sequence come back as zeros)
     auto gload = [&](int t) {
-        const int j0 = t * BN;
+        const uint32_t j0 = (uint32_t)(t * BN);
 #pragma unroll
         for (int c = 0; c < C::K_PER_T; ++c) {
             const int idx = c * C::NT + tid;
-            const int j = j0 + idx / C::NDVC;
-            kst[c] = j < s.S_kv ? *(const u32x4_t *)(kbase + (int64_t)j * p.k_stride + (idx % C::NDVC) * 8)
-                                : u32x4_t{0, 0, 0, 0};
+            kst[c] = buf_load16(kr, (j0 + idx / C::NDVC) * ks2 + (idx % C::NDVC) * 16);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = j0 + v_kg * 4 + r;
-            vst[r] = j < s.S_kv ? *(const u32x4_t *)(vbase + (int64_t)j * p.v_stride + v_dvc * 8)
-                                : u32x4_t{0, 0, 0, 0};
-        }
+        for (int r = 0; r < 4; ++r)
+            vst[r] = buf_load16(vr, (j0 + v_kg * 4 + r) * vs2 + v_dvc * 16);
     };
     auto stage = [&](int b) {
 #pragma unroll
@@ -211,70 +250,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
 #pragma unroll
     for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;
-    const float sc_silu = -p.alpha * kLog2e;
+    const float neg_alpha_log2e = -p.alpha * kLog2e;
     const float sc_soft = p.alpha * kLog2e;
+    const uint16_t *k_lane = &lds_k[0][r32 * C::KS + g * 8];
+    const uint16_t *v_lane = &lds_v[0][r32 * C::VS + 4 * g];
 
-    int buf = 0;
-    if (ntiles > 0) {
-        gload(bp.tiles.at(0));
-        stage(0);
-    }
+    // The loop body is straight-line (loads and stores are unconditional; the
+    // last iteration re-loads its own tile), so every load issued in one
+    // iteration is waited for only right before its LDS store.
+    gload(bp.tiles.at(0));
+    stage(0);
     __syncthreads();
 
+    int buf = 0;
     for (int n = 0; n < ntiles; ++n) {
         const int t = bp.tiles.at(n);
-        const bool has_next = n + 1 < ntiles;
-        if (has_next) gload(bp.tiles.at(n + 1));
+        gload(bp.tiles.at(n + 1 < ntiles ? n + 1 : n));
         const int j0 = t * BN;
         const int32_t st = tile_state(span, j0, j0 + BN);
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
         const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
 
         if (wave_any) {
-            // ---- S^T = K Q^T
+            const uint16_t *kp = k_lane + buf * C::KTILE;
+            const uint16_t *vp0 = v_lane + buf * C::VTILE;
+            // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
             f32x16_t sacc[C::NKB];
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-                sacc[kb] = f32x16_t{};
-                const uint16_t *kp = &lds_k[buf][(kb * 32 + r32) * C::KS + g * 8];
+            for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16_t{};
 #pragma unroll
-                for (int kk = 0; kk < C::KSTEPS; ++kk)
-                    sacc[kb] = E::mfma(*(const u32x4_t *)(kp + kk * 16), qreg[kk], sacc[kb]);
+            for (int kk = 0; kk < C::KSTEPS; ++kk) {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+                    sacc[kb] = E::mfma(*(const u32x4_t *)(kp + kb * 32 * C::KS + kk * 16), qreg[kk],
+                                       sacc[kb]);
             }
 
             // ---- mask + non-linearity; element i of block kb is key
             //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
-            u32x4_t pb[C::NKB][2];
             if constexpr (!SOFTMAX) {
+                if (wave_mask) {
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
+                    for (int kb = 0; kb < C::NKB; ++kb)
+                        silu_block<true>(sacc[kb], p.alpha, neg_alpha_log2e, span, j0 + kb * 32 + 4 * g);
+                } else {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float x = sacc[kb][i];
-                        // SiLU(alpha x) = alpha x / (1 + 2^(-alpha log2e x))
-                        float pv = (x * p.alpha) *
-                                   __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * sc_silu));
-                        if (wave_mask) {
-                            const int key = j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                            pv = span_visible(span, key) ? pv : 0.0f;
-                        }
-                        sacc[kb][i] = pv;
-                    }
+                    for (int kb = 0; kb < C::NKB; ++kb)
+                        silu_block<false>(sacc[kb], p.alpha, neg_alpha_log2e, span, 0);
                 }
             } else {
                 float mx = -INFINITY;
+                if (wave_mask) {
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
+                    for (int kb = 0; kb < C::NKB; ++kb)
+                        mx = fmaxf(mx, scale_block<true>(sacc[kb], sc_soft, span, j0 + kb * 32 + 4 * g));
+                } else {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float x = sacc[kb][i] * sc_soft;
-                        if (wave_mask) {
-                            const int key = j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                            x = span_visible(span, key) ? x : -INFINITY;
-                        }
-                        sacc[kb][i] = x;
-                        mx = fmaxf(mx, x);
-                    }
+                    for (int kb = 0; kb < C::NKB; ++kb)
+                        mx = fmaxf(mx, scale_block<false>(sacc[kb], sc_soft, span, 0));
                 }
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
                 const float m_new = fmaxf(m_run, mx);
@@ -298,17 +331,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
                 }
                 l_run += lsum;
             }
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    const int i0 = 8 * t2;
-                    pb[kb][t2] = u32x4_t{E::pack2(sacc[kb][i0 + 0], sacc[kb][i0 + 1]),
-                                         E::pack2(sacc[kb][i0 + 2], sacc[kb][i0 + 3]),
-                                         E::pack2(sacc[kb][i0 + 4], sacc[kb][i0 + 5]),
-                                         E::pack2(sacc[kb][i0 + 6], sacc[kb][i0 + 7])};
-                }
-            }
 
             // ---- O^T += V^T P^T; MFMA step (kb, t2) covers keys
             //      32kb + 16t2 + {4g..4g+3, 8+4g..8+4g+3} in both operands
@@ -316,18 +338,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
             for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2) {
+                    const int i0 = 8 * t2;
+                    const u32x4_t pb = {E::pack2(sacc[kb][i0 + 0], sacc[kb][i0 + 1]),
+                                        E::pack2(sacc[kb][i0 + 2], sacc[kb][i0 + 3]),
+                                        E::pack2(sacc[kb][i0 + 4], sacc[kb][i0 + 5]),
+                                        E::pack2(sacc[kb][i0 + 6], sacc[kb][i0 + 7])};
 #pragma unroll
                     for (int nb = 0; nb < C::NDB; ++nb) {
-                        const uint16_t *vp = &lds_v[buf][(nb * 32 + r32) * C::VS + kb * 32 + 16 * t2 + 4 * g];
+                        const uint16_t *vp = vp0 + nb * 32 * C::VS + kb * 32 + 16 * t2;
                         const u32x2_t a0 = *(const u32x2_t *)vp;
                         const u32x2_t a1 = *(const u32x2_t *)(vp + 8);
-                        oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb[kb][t2], oacc[nb]);
+                        oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb, oacc[nb]);
                     }
                 }
             }
         }
 
-        if (has_next) stage(buf ^ 1);
+        stage(buf ^ 1);
         __syncthreads();
         buf ^= 1;
     }
