@@ -13,12 +13,14 @@
 //   The accumulator gives lane l the scores of its own query against 16 keys
 //   of each 32-key block, so the mask is a per-lane interval test against the
 //   row's visible key set [0, ctx) U [lo, hi].
-//   O^T += V^T . P^T   A = V^T from LDS (V is transposed while staged), B = P^T
-//                   straight from the score registers: the key order inside
-//                   each 16-key MFMA step is permuted identically on both
-//                   operands, so no cross-lane shuffle is needed.
-// K and V tiles are double-buffered in LDS; the next tile's global loads are
-// issued before the current tile's MFMAs, one barrier per tile.
+//   O^T += V^T . P^T   A = V^T read from the row-major V tile with the gfx950
+//                   LDS transpose read (ds_read_b64_tr_b16), B = P^T straight
+//                   from the score registers: the key order inside each
+//                   16-key MFMA step is permuted identically on both operands,
+//                   so no cross-lane shuffle is needed.
+// K and V tiles go global -> LDS directly (buffer_load_dwordx4 ... lds, no
+// staging registers) into a two-stage ring; the next tile's loads are issued
+// before the current tile's MFMAs, one barrier per tile.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -68,22 +70,24 @@ struct Elem<HSTU_FP16> {
 };
 
 // Tile geometry for head dim D (= hdim_qk = hdim_v) and key-tile width BN.
+// K and V tiles sit in LDS row-major (BN rows of D elements, no padding); the
+// 16-byte chunks of each row are XOR-swizzled so the MFMA operand reads are
+// bank-conflict-free: K chunk c of row r is stored at chunk c ^ (r & 7) (eight
+// consecutive rows read the same chunk), V chunk c at c ^ 2(r & 3) (the
+// transposed reads touch four consecutive rows, two chunks each).
 template <int D, int BN>
 struct Tile {
     static constexpr int BM = 128;           // query rows per work-group
     static constexpr int NT = 256;           // threads
-    static constexpr int KS = D + 8;         // K tile row stride in LDS (elements)
-    static constexpr int VS = BN + 4;        // V^T tile row stride in LDS (elements)
-    static constexpr int KTILE = BN * KS;
-    static constexpr int VTILE = D * VS;
+    static constexpr int RB = D * 2;         // bytes per K or V row
+    static constexpr int CPR = D / 8;        // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BN * RB;
     static constexpr int KSTEPS = D / 16;    // MFMA k-steps of Q.K^T
     static constexpr int NKB = BN / 32;      // 32-key blocks per tile
     static constexpr int NDB = D / 32;       // 32-column blocks of the output
-    static constexpr int NDVC = D / 8;       // 16-byte chunks per row
-    static constexpr int K_PER_T = BN * NDVC / NT;  // K chunks staged per thread
-    static_assert(BN * D == 8192, "every thread stages one 4x8 V block and four K chunks");
-    static_assert((BN / 4) * NDVC == NT, "V staging covers the tile exactly");
-    static_assert(K_PER_T * NT == BN * NDVC, "K staging covers the tile exactly");
+    static constexpr int LOADS = BN * CPR / NT;  // 16-byte chunks each thread loads per tensor
+    static_assert(LOADS * NT == BN * CPR, "the loads cover the tile exactly");
+    static_assert(64 % CPR == 0, "one wave-load covers whole rows");
 };
 
 __device__ __forceinline__ int32_t wave_min(int32_t x) {
@@ -145,15 +149,16 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// SiLU on one 32-key block of scores, in place: p = alpha x / (1 + 2^(-alpha log2e x)),
-// zeroed outside the row's visible keys when MASK.
+// SiLU on one 32-key block of raw scores x = q.k, in place, without the factor
+// alpha: p = x / (1 + 2^(-alpha log2e x)) = SiLU(alpha x) / alpha; zeroed
+// outside the row's visible keys when MASK.
 template <bool MASK>
-__device__ __forceinline__ void silu_block(f32x16_t &x, float alpha, float neg_alpha_log2e,
-                                           const RowSpan &span, int key0) {
+__device__ __forceinline__ void silu_block(f32x16_t &x, float neg_alpha_log2e, const RowSpan &span,
+                                           int key0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float v = x[i];
-        float pv = (v * alpha) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * neg_alpha_log2e));
+        float pv = v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * neg_alpha_log2e));
         if constexpr (MASK) pv = span_visible(span, key0 + 8 * (i >> 2) + (i & 3)) ? pv : 0.0f;
         x[i] = pv;
     }
@@ -173,20 +178,67 @@ __device__ __forceinline__ float scale_block(f32x16_t &x, float sc, const RowSpa
     return mx;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
+// LDS byte address lds_wave + 16 i (lds_wave must be the same for the whole wave).
+// Issued through inline assembly so the compiler does not order later LDS reads
+// of the other stage behind it; completion is awaited explicitly (vmcnt(0) and a
+// barrier) before the stage is read.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4_t{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xffffu), (int32_t)bytes,
+                   0x00020000};
+}
+// M0 is a reserved register: the compiler neither preserves it across this
+// statement nor relies on it elsewhere in these kernels (gfx9+ LDS instructions
+// do not read M0; no other LDS-direct, message or indexed-register instruction
+// is used), so setting it here is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_to_lds(const i32x4_t &rsrc, uint32_t lds_wave, uint32_t off) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_wave), "v"(off), "s"(rsrc)
+        : "m0");
+}
+#pragma clang diagnostic pop
+
+// Transposed LDS read of 4 16-bit elements (gfx950): within each group of 16
+// lanes, lane i receives element i%4 of the 8-byte chunks addressed by lanes
+// 4r + i/4, r = 0..3.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint8_t *addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)addr));
+#else
+    return u32x2_t{0, 0};
+#endif
+}
+
+__device__ __forceinline__ void wait_all_loads() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every global->LDS load of this wave landed
+}
+
 template <int DT, int D, bool SOFTMAX, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
     using C = Tile<D, BN>;
     using E = Elem<DT>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][C::KTILE];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][C::VTILE];
+    // two stages of [K tile | V tile]
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * C::TILE_BYTES];
     __shared__ int32_t red[8];
 
     BlockPlan bp;
     if (!plan_block<BN>(p, SPLIT, bp, red)) return;
     const SeqGeom &s = bp.s;
     const RowSpan &span = bp.span;
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
     const int h = bp.it.h;
     const int ntiles = bp.tiles.count();
 
@@ -195,10 +247,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
                    vs2 = (uint32_t)p.v_stride * 2;
     const __amdgpu_buffer_rsrc_t qr =
         make_rsrc((const uint16_t *)p.q + s.q0 * p.q_stride + h * D, (uint32_t)s.S_q * qs2);
-    const __amdgpu_buffer_rsrc_t kr =
-        make_rsrc((const uint16_t *)p.k + s.kv0 * p.k_stride + h * D, (uint32_t)s.S_kv * ks2);
-    const __amdgpu_buffer_rsrc_t vr =
-        make_rsrc((const uint16_t *)p.v + s.kv0 * p.v_stride + h * D, (uint32_t)s.S_kv * vs2);
+    const i32x4_t kr =
+        make_rsrc_words((const uint16_t *)p.k + s.kv0 * p.k_stride + h * D, (uint32_t)s.S_kv * ks2);
+    const i32x4_t vr =
+        make_rsrc_words((const uint16_t *)p.v + s.kv0 * p.v_stride + h * D, (uint32_t)s.S_kv * vs2);
 
     // ---- Q^T operand: lane holds d = 16*kk + 8*g .. +7 of its row
     u32x4_t qreg[C::KSTEPS];
@@ -206,45 +258,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
     for (int kk = 0; kk < C::KSTEPS; ++kk)
         qreg[kk] = buf_load16(qr, (uint32_t)bp.row * qs2 + (kk * 16 + g * 8) * 2);
 
-    // ---- staging assignment of this thread
-    // V: a 4-key x 8-column block; within each 16 lanes (dvc_lo, kg_lo) are
-    // distinct so the transposed LDS writes spread over the banks.
-    const int v_dvc = ((tid >> 4) % (C::NDVC / 4)) * 4 + (tid & 3);
-    const int v_kg = ((tid >> 4) / (C::NDVC / 4)) * 4 + ((tid >> 2) & 3);
-    u32x4_t kst[C::K_PER_T];
-    u32x4_t vst[4];
-
-    // loads of key tile t (rows past the sequence come back as zeros)
-    auto gload = [&](int t) {
+    // ---- global -> LDS loads of key tile t into stage b.  Wave-load c of wave w
+    //      fills physical chunks [(4c + w) 64, +64); the chunk a lane lands on
+    //      decides which logical chunk (swizzle undone) it fetches.
+    uint32_t ld_row[C::LOADS], ld_kchunk[C::LOADS], ld_vchunk[C::LOADS];
+#pragma unroll
+    for (int c = 0; c < C::LOADS; ++c) {
+        const int phys = (c * 4 + wave) * 64 + lane;
+        const int row = phys / C::CPR, pc = phys % C::CPR;
+        ld_row[c] = (uint32_t)row;
+        ld_kchunk[c] = (uint32_t)(pc ^ (row & 7)) * 16;
+        ld_vchunk[c] = (uint32_t)(pc ^ (2 * (row & 3))) * 16;
+    }
+    // LDS byte address of this wave's first landing slot (wave-uniform)
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] +
+                              (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024;
+    auto issue_loads = [&](int t, int b) {
         const uint32_t j0 = (uint32_t)(t * BN);
 #pragma unroll
-        for (int c = 0; c < C::K_PER_T; ++c) {
-            const int idx = c * C::NT + tid;
-            kst[c] = buf_load16(kr, (j0 + idx / C::NDVC) * ks2 + (idx % C::NDVC) * 16);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            vst[r] = buf_load16(vr, (j0 + v_kg * 4 + r) * vs2 + v_dvc * 16);
-    };
-    auto stage = [&](int b) {
-#pragma unroll
-        for (int c = 0; c < C::K_PER_T; ++c) {
-            const int idx = c * C::NT + tid;
-            *(u32x4_t *)&lds_k[b][(idx / C::NDVC) * C::KS + (idx % C::NDVC) * 8] = kst[c];
-        }
-        // transpose the 4x8 block: column e of the 4 keys becomes 8 contiguous bytes
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-#pragma unroll
-            for (int odd = 0; odd < 2; ++odd) {
-                const uint32_t sel = odd ? 0x07060302u : 0x05040100u;
-                u32x2_t col;
-                col.x = __builtin_amdgcn_perm(vst[1][w], vst[0][w], sel);
-                col.y = __builtin_amdgcn_perm(vst[3][w], vst[2][w], sel);
-                *(u32x2_t *)&lds_v[b][(v_dvc * 8 + 2 * w + odd) * C::VS + v_kg * 4] = col;
-            }
+        for (int c = 0; c < C::LOADS; ++c) {
+            const uint32_t dst = lds_base + b * (2 * C::TILE_BYTES) + c * 4 * 1024;
+            load_to_lds(kr, dst, (j0 + ld_row[c]) * ks2 + ld_kchunk[c]);
+            load_to_lds(vr, dst + C::TILE_BYTES, (j0 + ld_row[c]) * vs2 + ld_vchunk[c]);
         }
     };
+
+    // ---- per-lane LDS read addresses (stage 0; stage 1 adds 2 * TILE_BYTES)
+    // K operand of S^T = K Q^T: row 32kb + r32, logical chunk 2kk + g
+    uint32_t k_addr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        k_addr[m] = (uint32_t)(r32 * C::RB + (((2 * m + g) ^ (r32 & 7)) * 16));
+    // V^T operand (transposed read): row K0 + 4g + (i/4), columns 32nb + 16hb + 4(i%4)
+    const int i16 = lane & 15, hb = (lane >> 4) & 1;
+    const int vy = 2 * ((i16 >> 2) & 3);
+    uint32_t v_addr[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+        v_addr[b2] = (uint32_t)(C::TILE_BYTES + (4 * g + (i16 >> 2)) * C::RB +
+                                (((4 * b2 + 2 * hb + ((i16 & 3) >> 1)) ^ vy) * 16) + (i16 & 1) * 8);
 
     f32x16_t oacc[C::NDB];
 #pragma unroll
@@ -252,28 +304,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
     float m_run = -INFINITY, l_run = 0.f;
     const float neg_alpha_log2e = -p.alpha * kLog2e;
     const float sc_soft = p.alpha * kLog2e;
-    const uint16_t *k_lane = &lds_k[0][r32 * C::KS + g * 8];
-    const uint16_t *v_lane = &lds_v[0][r32 * C::VS + 4 * g];
+    const uint8_t *lds0 = &lds[0][0];
 
-    // The loop body is straight-line (loads and stores are unconditional; the
-    // last iteration re-loads its own tile), so every load issued in one
-    // iteration is waited for only right before its LDS store.
-    gload(bp.tiles.at(0));
-    stage(0);
+    if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
+    wait_all_loads();
     __syncthreads();
 
-    int buf = 0;
     for (int n = 0; n < ntiles; ++n) {
-        const int t = bp.tiles.at(n);
-        gload(bp.tiles.at(n + 1 < ntiles ? n + 1 : n));
-        const int j0 = t * BN;
+        const int buf = n & 1;
+        if (n + 1 < ntiles) issue_loads(bp.tiles.at(n + 1), buf ^ 1);
+        const int j0 = bp.tiles.at(n) * BN;
         const int32_t st = tile_state(span, j0, j0 + BN);
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
         const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
 
         if (wave_any) {
-            const uint16_t *kp = k_lane + buf * C::KTILE;
-            const uint16_t *vp0 = v_lane + buf * C::VTILE;
+            const uint8_t *stage = lds0 + buf * (2 * C::TILE_BYTES);
             // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
             f32x16_t sacc[C::NKB];
 #pragma unroll
@@ -281,22 +327,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
 #pragma unroll
             for (int kk = 0; kk < C::KSTEPS; ++kk) {
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-                    sacc[kb] = E::mfma(*(const u32x4_t *)(kp + kb * 32 * C::KS + kk * 16), qreg[kk],
-                                       sacc[kb]);
+                for (int kb = 0; kb < C::NKB; ++kb) {
+                    const uint8_t *ka = stage + k_addr[kk & 3] + kb * 32 * C::RB + (kk >> 2) * 128;
+                    sacc[kb] = E::mfma(*(const u32x4_t *)ka, qreg[kk], sacc[kb]);
+                }
             }
 
             // ---- mask + non-linearity; element i of block kb is key
             //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
             if constexpr (!SOFTMAX) {
+                // p = x sigmoid(alpha x); the factor alpha of SiLU(alpha x) goes into the epilogue
                 if (wave_mask) {
 #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb)
-                        silu_block<true>(sacc[kb], p.alpha, neg_alpha_log2e, span, j0 + kb * 32 + 4 * g);
+                        silu_block<true>(sacc[kb], neg_alpha_log2e, span, j0 + kb * 32 + 4 * g);
                 } else {
 #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb)
-                        silu_block<false>(sacc[kb], p.alpha, neg_alpha_log2e, span, 0);
+                        silu_block<false>(sacc[kb], neg_alpha_log2e, span, 0);
                 }
             } else {
                 float mx = -INFINITY;
@@ -343,24 +391,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
                                         E::pack2(sacc[kb][i0 + 2], sacc[kb][i0 + 3]),
                                         E::pack2(sacc[kb][i0 + 4], sacc[kb][i0 + 5]),
                                         E::pack2(sacc[kb][i0 + 6], sacc[kb][i0 + 7])};
+                    const int key0 = kb * 32 + 16 * t2;
 #pragma unroll
                     for (int nb = 0; nb < C::NDB; ++nb) {
-                        const uint16_t *vp = vp0 + nb * 32 * C::VS + kb * 32 + 16 * t2;
-                        const u32x2_t a0 = *(const u32x2_t *)vp;
-                        const u32x2_t a1 = *(const u32x2_t *)(vp + 8);
+                        const uint8_t *va = stage + v_addr[nb & 1] + key0 * C::RB + (nb >> 1) * 128;
+                        const u32x2_t a0 = lds_read_tr16(va);
+                        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RB);
                         oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb, oacc[nb]);
                     }
                 }
             }
         }
 
-        stage(buf ^ 1);
+        wait_all_loads();
         __syncthreads();
-        buf ^= 1;
     }
 
     // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
-    float scale = s.attn_scale;
+    float scale = s.attn_scale * p.alpha;
     float lse_val = 0.f;
     if constexpr (SOFTMAX) {
         const float l = l_run + __shfl_xor(l_run, 32);
