@@ -225,6 +225,78 @@ __device__ __forceinline__ void wait_all_loads() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every global->LDS load of this wave landed
 }
 
+// SiLU of one score without the factor alpha (see silu_block), unmasked.
+__device__ __forceinline__ float silu_raw(float v, float neg_alpha_log2e) {
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * neg_alpha_log2e));
+}
+
+// One unmasked SiLU key tile of 64 keys (two 32-key blocks) for one wave,
+// software-pipelined so that the wave keeps the matrix pipe and the VALU busy
+// together.  Written in issue order, one step per MFMA, with scheduling fences
+// (sched_barrier) between steps so the compiler keeps the interleave:
+//   A: block 0 scores (8 MFMAs)            + block 1 K operand reads
+//   B: block 1 scores (8 MFMAs)            + block 0 SiLU (2 scores/step) + block 0 V^T reads
+//   C: block 0 P.V    (8 MFMAs)            + block 1 SiLU (2 scores/step) + block 1 V^T reads
+//   D: block 1 P.V    (8 MFMAs)
+// The fences change the instruction order only, never the arithmetic.
+template <class E, int D>
+__device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const uint32_t *k_addr,
+                                                    const uint32_t *v_addr, const u32x4_t *qreg,
+                                                    f32x16_t *oacc, float neg_alpha_log2e) {
+    using C = Tile<D, 64>;
+    static_assert(C::NKB == 2 && C::KSTEPS == 8 && C::NDB == 4, "hdim 128, 64-key tiles");
+    auto kread = [&](int kb, int kk) {
+        return *(const u32x4_t *)(stage + k_addr[kk & 3] + kb * 32 * C::RB + (kk >> 2) * 128);
+    };
+    // P.V step i of block kb: t2 = i / 4 (16-key half), nb = i % 4 (32-column block)
+    auto vread = [&](int kb, int i) {
+        const int t2 = i >> 2, nb = i & 3;
+        const uint8_t *va = stage + v_addr[nb & 1] + (kb * 32 + 16 * t2) * C::RB + (nb >> 1) * 128;
+        const u32x2_t a0 = lds_read_tr16(va);
+        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RB);
+        return u32x4_t{a0.x, a0.y, a1.x, a1.y};
+    };
+    auto pack8 = [&](const f32x16_t &x, int i0) {
+        return u32x4_t{E::pack2(x[i0 + 0], x[i0 + 1]), E::pack2(x[i0 + 2], x[i0 + 3]),
+                       E::pack2(x[i0 + 4], x[i0 + 5]), E::pack2(x[i0 + 6], x[i0 + 7])};
+    };
+
+    f32x16_t s0 = {}, s1 = {};
+    u32x4_t op0[8], op1[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) op0[kk] = kread(0, kk);
+    // A
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        s0 = E::mfma(op0[kk], qreg[kk], s0);
+        op1[kk] = kread(1, kk);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // B
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        s1 = E::mfma(op1[kk], qreg[kk], s1);
+        op0[kk] = vread(0, kk);
+        s0[2 * kk] = silu_raw(s0[2 * kk], neg_alpha_log2e);
+        s0[2 * kk + 1] = silu_raw(s0[2 * kk + 1], neg_alpha_log2e);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const u32x4_t p0[2] = {pack8(s0, 0), pack8(s0, 8)};
+    // C
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        oacc[i & 3] = E::mfma(op0[i], p0[i >> 2], oacc[i & 3]);
+        op1[i] = vread(1, i);
+        s1[2 * i] = silu_raw(s1[2 * i], neg_alpha_log2e);
+        s1[2 * i + 1] = silu_raw(s1[2 * i + 1], neg_alpha_log2e);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const u32x4_t p1[2] = {pack8(s1, 0), pack8(s1, 8)};
+    // D
+#pragma unroll
+    for (int i = 0; i < 8; ++i) oacc[i & 3] = E::mfma(op1[i], p1[i >> 2], oacc[i & 3]);
+}
+
 template <int DT, int D, bool SOFTMAX, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
@@ -318,6 +390,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
         const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
 
+        if constexpr (!SOFTMAX && D == 128) {
+            if (wave_any && !wave_mask) {
+                silu_tile_pipelined<E, D>(lds0 + buf * (2 * C::TILE_BYTES), k_addr, v_addr, qreg, oacc,
+                                          neg_alpha_log2e);
+                wait_all_loads();
+                __syncthreads();
+                continue;
+            }
+        }
         if (wave_any) {
             const uint8_t *stage = lds0 + buf * (2 * C::TILE_BYTES);
             // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
