@@ -71,10 +71,11 @@ struct Elem<HSTU_FP16> {
 
 // Tile geometry for head dim D (= hdim_qk = hdim_v) and key-tile width BN.
 // K and V tiles sit in LDS row-major (BN rows of D elements, no padding); the
-// 16-byte chunks of each row are XOR-swizzled so the MFMA operand reads are
-// bank-conflict-free: K chunk c of row r is stored at chunk c ^ (r & 7) (eight
-// consecutive rows read the same chunk), V chunk c at c ^ 2(r & 3) (the
-// transposed reads touch four consecutive rows, two chunks each).
+// 16-byte chunks of each row are XOR-swizzled against LDS bank conflicts of the
+// MFMA operand reads (tables chosen by timing the exact read patterns on the
+// device): K chunk c of row r is stored at chunk c ^ (r & 15) (the 32 lanes of
+// a half-wave read one chunk of 32 consecutive rows), V chunk c at c ^ 4(r & 3)
+// (the transposed reads touch four consecutive rows, 64 bytes each).
 template <int D, int BN>
 struct Tile {
     static constexpr int BM = 128;           // query rows per work-group
@@ -230,7 +231,9 @@ __device__ __forceinline__ float silu_raw(float v, float neg_alpha_log2e) {
     return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * neg_alpha_log2e));
 }
 
-// One unmasked SiLU key tile of 64 keys (two 32-key blocks) for one wave,
+// One unmasked SiLU key tile of 64 keys (two 32-key blocks) for one wave at
+// hdim 128 (k_addr: 8 lane offsets, one per k-step; v_addr: 4, one per 32-column
+// block),
 // software-pipelined so that the wave keeps the matrix pipe and the VALU busy
 // together.  Written in issue order, one step per MFMA, with scheduling fences
 // (sched_barrier) between steps so the compiler keeps the interleave:
@@ -246,12 +249,12 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     using C = Tile<D, 64>;
     static_assert(C::NKB == 2 && C::KSTEPS == 8 && C::NDB == 4, "hdim 128, 64-key tiles");
     auto kread = [&](int kb, int kk) {
-        return *(const u32x4_t *)(stage + k_addr[kk & 3] + kb * 32 * C::RB + (kk >> 2) * 128);
+        return *(const u32x4_t *)(stage + k_addr[kk] + kb * 32 * C::RB);
     };
     // P.V step i of block kb: t2 = i / 4 (16-key half), nb = i % 4 (32-column block)
     auto vread = [&](int kb, int i) {
         const int t2 = i >> 2, nb = i & 3;
-        const uint8_t *va = stage + v_addr[nb & 1] + (kb * 32 + 16 * t2) * C::RB + (nb >> 1) * 128;
+        const uint8_t *va = stage + v_addr[nb] + (kb * 32 + 16 * t2) * C::RB;
         const u32x2_t a0 = lds_read_tr16(va);
         const u32x2_t a1 = lds_read_tr16(va + 8 * C::RB);
         return u32x4_t{a0.x, a0.y, a1.x, a1.y};
@@ -301,6 +304,10 @@ template <int DT, int D, bool SOFTMAX, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
     using C = Tile<D, BN>;
+    // K swizzle over the low 4 chunk bits (3 when a row has only 8 chunks);
+    // V swizzle 4(r & 3) needs 16 chunks per row, 2(r & 3) with 8
+    constexpr int kKSwz = C::CPR >= 16 ? 15 : 7;
+    constexpr int kVSwz = C::CPR >= 16 ? 4 : 2;
     using E = Elem<DT>;
     // two stages of [K tile | V tile]
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * C::TILE_BYTES];
@@ -339,8 +346,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
         const int phys = (c * 4 + wave) * 64 + lane;
         const int row = phys / C::CPR, pc = phys % C::CPR;
         ld_row[c] = (uint32_t)row;
-        ld_kchunk[c] = (uint32_t)(pc ^ (row & 7)) * 16;
-        ld_vchunk[c] = (uint32_t)(pc ^ (2 * (row & 3))) * 16;
+        ld_kchunk[c] = (uint32_t)(pc ^ (row & kKSwz)) * 16;
+        ld_vchunk[c] = (uint32_t)(pc ^ (kVSwz * (row & 3))) * 16;
     }
     // LDS byte address of this wave's first landing slot (wave-uniform)
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] +
@@ -357,16 +364,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
 
     // ---- per-lane LDS read addresses (stage 0; stage 1 adds 2 * TILE_BYTES)
     // K operand of S^T = K Q^T: row 32kb + r32, logical chunk 2kk + g
-    uint32_t k_addr[4];
+    // (the swizzle mixes the low log2(NKA)+1 chunk bits, so NKA k-steps get their own
+    //  lane offsets and later k-steps repeat them one swizzle period further on)
+    constexpr int NKA = (kKSwz + 1) / 2, NVA = kVSwz == 4 ? 4 : 2;
+    uint32_t k_addr[NKA];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        k_addr[m] = (uint32_t)(r32 * C::RB + (((2 * m + g) ^ (r32 & 7)) * 16));
+    for (int m = 0; m < NKA; ++m)
+        k_addr[m] = (uint32_t)(r32 * C::RB + (((2 * m + g) ^ (r32 & kKSwz)) * 16));
     // V^T operand (transposed read): row K0 + 4g + (i/4), columns 32nb + 16hb + 4(i%4)
     const int i16 = lane & 15, hb = (lane >> 4) & 1;
-    const int vy = 2 * ((i16 >> 2) & 3);
-    uint32_t v_addr[2];
+    const int vy = kVSwz * ((i16 >> 2) & 3);
+    uint32_t v_addr[NVA];
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int b2 = 0; b2 < NVA; ++b2)
         v_addr[b2] = (uint32_t)(C::TILE_BYTES + (4 * g + (i16 >> 2)) * C::RB +
                                 (((4 * b2 + 2 * hb + ((i16 & 3) >> 1)) ^ vy) * 16) + (i16 & 1) * 8);
 
@@ -409,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
             for (int kk = 0; kk < C::KSTEPS; ++kk) {
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb) {
-                    const uint8_t *ka = stage + k_addr[kk & 3] + kb * 32 * C::RB + (kk >> 2) * 128;
+                    const uint8_t *ka = stage + k_addr[kk % NKA] + kb * 32 * C::RB + (kk / NKA) * (NKA * 32);
                     sacc[kb] = E::mfma(*(const u32x4_t *)ka, qreg[kk], sacc[kb]);
                 }
             }
@@ -475,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
                     const int key0 = kb * 32 + 16 * t2;
 #pragma unroll
                     for (int nb = 0; nb < C::NDB; ++nb) {
-                        const uint8_t *va = stage + v_addr[nb & 1] + key0 * C::RB + (nb >> 1) * 128;
+                        const uint8_t *va = stage + v_addr[nb % NVA] + key0 * C::RB + (nb / NVA) * (NVA * 64);
                         const u32x2_t a0 = lds_read_tr16(va);
                         const u32x2_t a1 = lds_read_tr16(va + 8 * C::RB);
                         oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb, oacc[nb]);
