@@ -42,8 +42,10 @@ def kernel_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the kernel takes ~1 ms: the default warm-up (~50 ms of back-to-back launches)
+    # lets the GPU clock settle, which the first few launches show they need
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
@@ -164,7 +166,8 @@ def main():
                    "splits": splits, "schedule": args.schedule,
                    "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"},
         "wall_s_timed": round(wall, 3),
     }
     if args.cpu_seconds > 0:
