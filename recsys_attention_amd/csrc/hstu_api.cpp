@@ -129,7 +129,8 @@ void fill_params(const hstu_fwd_args_t *a, int32_t num_splits, hstu::KernelParam
     p.cross = a->cross;
     p.causal = a->causal;
     p.total_rows = (int32_t)rows_q(a);
-    p.num_qt = (a->seqlen_q + hstu::kBlockM - 1) / hstu::kBlockM;
+    const int bm = hstu::block_m_for(a->hdim_qk);
+    p.num_qt = (a->seqlen_q + bm - 1) / bm;
     const int64_t bh = (int64_t)a->batch * a->nhead;
     p.bh_pad = (int32_t)((bh + 7) / 8 * 8);
     p.num_splits = num_splits;

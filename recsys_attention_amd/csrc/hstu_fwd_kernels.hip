@@ -4,7 +4,7 @@
 // (s = alpha * q.k, functional mask, SiLU * attn_scale or attn_scale * softmax,
 // o = p @ v) and "Split-KV" (key axis cut across work-groups + combine pass).
 //
-// Work-group = 256 threads = 4 waves; it owns BM = 128 query rows of one
+// Work-group = 4 waves (waves_for); it owns 32 query rows per wave of one
 // (sequence, head), 32 rows per wave.  Within a wave, lane l owns query row
 // l % 32 and half of each key block (lane group g = l / 32):
 //   S^T = K . Q^T   v_mfma_f32_32x32x16_{bf16,f16}: A = K tile from LDS
@@ -76,10 +76,10 @@ struct Elem<HSTU_FP16> {
 // device): K chunk c of row r is stored at chunk c ^ (r & 15) (the 32 lanes of
 // a half-wave read one chunk of 32 consecutive rows), V chunk c at c ^ 4(r & 3)
 // (the transposed reads touch four consecutive rows, 64 bytes each).
-template <int D, int BN>
+template <int D, int BN, int NW = 4>
 struct Tile {
-    static constexpr int BM = 128;           // query rows per work-group
-    static constexpr int NT = 256;           // threads
+    static constexpr int BM = 32 * NW;       // query rows per work-group (32 per wave)
+    static constexpr int NT = 64 * NW;       // threads
     static constexpr int RB = D * 2;         // bytes per K or V row
     static constexpr int CPR = D / 8;        // 16-byte chunks per row
     static constexpr int TILE_BYTES = BN * RB;
@@ -112,18 +112,18 @@ struct BlockPlan {
     int32_t row;  // row inside the sequence owned by this lane
 };
 
-template <int BN>
+template <int BN, int NW>
 __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, BlockPlan &bp,
                                            int32_t *red) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     bp.it = decode_work(p, blockIdx.x);
     if (!bp.it.valid) return false;
     bp.s = seq_geom(p, bp.it.b);
-    const int32_t r0 = bp.it.qt * 128;
+    const int32_t r0 = bp.it.qt * (32 * NW);
     if (r0 >= bp.s.S_q) return false;
     bp.row = r0 + wave * 32 + (lane & 31);
     bp.span = row_span(bp.s, p.causal, bp.row);
-    // union of the band parts over the 128 rows
+    // union of the band parts over the work-group's rows
     int32_t lo = wave_min(bp.span.lo);
     int32_t hi = wave_max(bp.span.hi);
     if (lane == 0) {
@@ -131,8 +131,13 @@ __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, Bl
         red[2 * wave + 1] = hi;
     }
     __syncthreads();
-    lo = imin(imin(red[0], red[2]), imin(red[4], red[6]));
-    hi = imax(imax(red[1], red[3]), imax(red[5], red[7]));
+    lo = red[0];
+    hi = red[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        lo = imin(lo, red[2 * w]);
+        hi = imax(hi, red[2 * w + 1]);
+    }
     int32_t tb = 0, te = (bp.s.S_kv + BN - 1) / BN;
     if (split) split_range(bp.s.S_kv, BN, p.num_splits, bp.it.sp, &tb, &te);
     // rows r0.. exist (r0 < S_q), so the context tiles are needed
@@ -190,9 +195,12 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 // barrier) before the stage is read.
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4_t make_rsrc_words(const void *base, uint32_t bytes) {
+    // the words are work-group uniform; readfirstlane keeps them in SGPRs, where
+    // the buffer instruction needs its descriptor
     const uint64_t a = (uint64_t)base;
-    return i32x4_t{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xffffu), (int32_t)bytes,
-                   0x00020000};
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a),
+                   __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xffffu)),
+                   __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000};
 }
 // M0 is a reserved register: the compiler neither preserves it across this
 // statement nor relies on it elsewhere in these kernels (gfx9+ LDS instructions
@@ -241,11 +249,13 @@ __device__ __forceinline__ float silu_raw(float v, float neg_alpha_log2e) {
 //   B: block 1 scores (8 MFMAs)            + block 0 SiLU (2 scores/step) + block 0 V^T reads
 //   C: block 0 P.V    (8 MFMAs)            + block 1 SiLU (2 scores/step) + block 1 V^T reads
 //   D: block 1 P.V    (8 MFMAs)
+// The next tile's global->LDS loads (issue_load(0..7)) are spread over phase A.
 // The fences change the instruction order only, never the arithmetic.
-template <class E, int D>
+template <class E, int D, class IssueLoad>
 __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const uint32_t *k_addr,
                                                     const uint32_t *v_addr, const u32x4_t *qreg,
-                                                    f32x16_t *oacc, float neg_alpha_log2e) {
+                                                    f32x16_t *oacc, float neg_alpha_log2e,
+                                                    IssueLoad &&issue_load) {
     using C = Tile<D, 64>;
     static_assert(C::NKB == 2 && C::KSTEPS == 8 && C::NDB == 4, "hdim 128, 64-key tiles");
     auto kread = [&](int kb, int kk) {
@@ -268,11 +278,12 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     u32x4_t op0[8], op1[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) op0[kk] = kread(0, kk);
-    // A
+    // A (also issues the next tile's eight global->LDS loads, one per step)
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
         s0 = E::mfma(op0[kk], qreg[kk], s0);
         op1[kk] = kread(1, kk);
+        issue_load(kk);
         __builtin_amdgcn_sched_barrier(0);
     }
     // B
@@ -301,9 +312,10 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
 }
 
 template <int DT, int D, bool SOFTMAX, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
+__global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
-    using C = Tile<D, BN>;
+    constexpr int NW = waves_for(D);
+    using C = Tile<D, BN, NW>;
     // K swizzle over the low 4 chunk bits (3 when a row has only 8 chunks);
     // V swizzle 4(r & 3) needs 16 chunks per row, 2(r & 3) with 8
     constexpr int kKSwz = C::CPR >= 16 ? 15 : 7;
@@ -311,10 +323,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
     using E = Elem<DT>;
     // two stages of [K tile | V tile]
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * C::TILE_BYTES];
-    __shared__ int32_t red[8];
+    __shared__ int32_t red[2 * NW];
 
     BlockPlan bp;
-    if (!plan_block<BN>(p, SPLIT, bp, red)) return;
+    if (!plan_block<BN, NW>(p, SPLIT, bp, red)) return;
     const SeqGeom &s = bp.s;
     const RowSpan &span = bp.span;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
@@ -343,7 +355,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
     uint32_t ld_row[C::LOADS], ld_kchunk[C::LOADS], ld_vchunk[C::LOADS];
 #pragma unroll
     for (int c = 0; c < C::LOADS; ++c) {
-        const int phys = (c * 4 + wave) * 64 + lane;
+        const int phys = (c * NW + wave) * 64 + lane;
         const int row = phys / C::CPR, pc = phys % C::CPR;
         ld_row[c] = (uint32_t)row;
         ld_kchunk[c] = (uint32_t)(pc ^ (row & kKSwz)) * 16;
@@ -352,14 +364,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
     // LDS byte address of this wave's first landing slot (wave-uniform)
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] +
                               (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024;
-    auto issue_loads = [&](int t, int b) {
+    // load idx of key tile t into stage b: idx < LOADS are K chunks, the rest V
+    auto issue_one = [&](int t, int b, int idx) {
         const uint32_t j0 = (uint32_t)(t * BN);
-#pragma unroll
-        for (int c = 0; c < C::LOADS; ++c) {
-            const uint32_t dst = lds_base + b * (2 * C::TILE_BYTES) + c * 4 * 1024;
+        const int c = idx % C::LOADS;
+        const uint32_t dst = lds_base + b * (2 * C::TILE_BYTES) + c * NW * 1024;
+        if (idx < C::LOADS)
             load_to_lds(kr, dst, (j0 + ld_row[c]) * ks2 + ld_kchunk[c]);
+        else
             load_to_lds(vr, dst + C::TILE_BYTES, (j0 + ld_row[c]) * vs2 + ld_vchunk[c]);
-        }
+    };
+    auto issue_loads = [&](int t, int b) {
+#pragma unroll
+        for (int idx = 0; idx < 2 * C::LOADS; ++idx) issue_one(t, b, idx);
     };
 
     // ---- per-lane LDS read addresses (stage 0; stage 1 adds 2 * TILE_BYTES)
@@ -394,7 +411,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
 
     for (int n = 0; n < ntiles; ++n) {
         const int buf = n & 1;
-        if (n + 1 < ntiles) issue_loads(bp.tiles.at(n + 1), buf ^ 1);
+        const bool has_next = n + 1 < ntiles;
+        const int t_next = bp.tiles.at(has_next ? n + 1 : n);
         const int j0 = bp.tiles.at(n) * BN;
         const int32_t st = tile_state(span, j0, j0 + BN);
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
@@ -403,12 +421,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 
         if constexpr (!SOFTMAX && D == 128) {
             if (wave_any && !wave_mask) {
                 silu_tile_pipelined<E, D>(lds0 + buf * (2 * C::TILE_BYTES), k_addr, v_addr, qreg, oacc,
-                                          neg_alpha_log2e);
+                                          neg_alpha_log2e, [&](int idx) {
+                                              if (has_next && idx < 2 * C::LOADS)
+                                                  issue_one(t_next, buf ^ 1, idx);
+                                          });
                 wait_all_loads();
                 __syncthreads();
                 continue;
             }
         }
+        if (has_next) issue_loads(t_next, buf ^ 1);
         if (wave_any) {
             const uint8_t *stage = lds0 + buf * (2 * C::TILE_BYTES);
             // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
@@ -604,11 +626,11 @@ __global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D
 // Visible pairs inside the scheduled key tiles, counted with the forward
 // kernel's own plan and predicate (the same lane -> (row, key) assignment and
 // the same full-tile shortcut).
-template <int BN>
-__global__ __launch_bounds__(256) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
-    __shared__ int32_t red[8];
+template <int BN, int NW>
+__global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
+    __shared__ int32_t red[2 * NW];
     BlockPlan bp;
-    if (!plan_block<BN>(p, false, bp, red)) return;
+    if (!plan_block<BN, NW>(p, false, bp, red)) return;
     const int lane = threadIdx.x & 63, g = lane >> 5;
     unsigned long long mine = 0;
     const int ntiles = bp.tiles.count();
@@ -638,7 +660,7 @@ template <int DT, int D, bool SOFTMAX, bool SPLIT>
 static hipError_t launch_one(const KernelParams &p, hipStream_t stream) {
     const int64_t grid = grid_size(p);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT>), dim3((unsigned)grid), dim3(256), 0,
+    hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT>), dim3((unsigned)grid), dim3(64 * waves_for(D)), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -688,9 +710,9 @@ hipError_t launch_count(const KernelParams &p, int D, unsigned long long *count,
     const int64_t grid = grid_size(p);
     if (grid > 0) {
         switch (D) {
-            case 64: hipLaunchKernelGGL(hstu_count_kernel<key_tile_for(64)>, dim3((unsigned)grid), dim3(256), 0, stream, p, count); break;
-            case 128: hipLaunchKernelGGL(hstu_count_kernel<key_tile_for(128)>, dim3((unsigned)grid), dim3(256), 0, stream, p, count); break;
-            case 256: hipLaunchKernelGGL(hstu_count_kernel<key_tile_for(256)>, dim3((unsigned)grid), dim3(256), 0, stream, p, count); break;
+            case 64: hipLaunchKernelGGL((hstu_count_kernel<key_tile_for(64), waves_for(64)>), dim3((unsigned)grid), dim3(64 * waves_for(64)), 0, stream, p, count); break;
+            case 128: hipLaunchKernelGGL((hstu_count_kernel<key_tile_for(128), waves_for(128)>), dim3((unsigned)grid), dim3(64 * waves_for(128)), 0, stream, p, count); break;
+            case 256: hipLaunchKernelGGL((hstu_count_kernel<key_tile_for(256), waves_for(256)>), dim3((unsigned)grid), dim3(64 * waves_for(256)), 0, stream, p, count); break;
             default: return hipErrorInvalidValue;
         }
     }
