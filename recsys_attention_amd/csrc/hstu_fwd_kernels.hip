@@ -570,13 +570,19 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     }
 }
 
-// Split-KV combine: one thread per (row, head, 4 columns).
+// Split-KV combine: one thread per (row, head, 4 columns); the 32 threads of a
+// (row, head) read one contiguous 512-byte slice of every split's partial row.
 //   SiLU:    o = sum_c o_c
 //   softmax: lse = ln sum_c exp(lse_c); o = sum_c exp(lse_c - lse) o_c
 //            (a row no split sees: o = 0, lse = -inf)
+// HBM-bound: the splits are read in unrolled chunks of CH, every load of a
+// chunk (LSEs and partial rows) issued before any is used, and the softmax
+// weights are folded in with a running maximum, so the whole reduction is one
+// pass with CH loads per thread in flight.
 template <int DT, bool SOFTMAX>
 __global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D) {
     using E = Elem<DT>;
+    constexpr int CH = 16;
     const int nchunk = D / 4;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)p.total_rows * p.H * nchunk;
@@ -584,25 +590,50 @@ __global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D
     const int chunk = (int)(idx % nchunk);
     const int64_t rh = idx / nchunk;  // row * H + h
     const int64_t split_stride = (int64_t)p.total_rows * p.H;
+    const float *po = p.part_o + rh * D + chunk * 4;
+    const int64_t po_stride = split_stride * D;
+    const float *pl = p.part_lse + rh;
+    const int ns = p.num_splits;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float lse = 0.f;
-    if constexpr (!SOFTMAX) {
-        for (int c = 0; c < p.num_splits; ++c)
-            acc += *(const f32x4_t *)(p.part_o + (c * split_stride + rh) * D + chunk * 4);
-    } else {
-        float mx = -INFINITY;
-        for (int c = 0; c < p.num_splits; ++c) mx = fmaxf(mx, p.part_lse[c * split_stride + rh]);
-        if (mx == -INFINITY) {
-            lse = -INFINITY;
+    float m = -INFINITY, sum = 0.f;  // softmax: running max of the LSEs, sum of exp(lse_c - m)
+    for (int c0 = 0; c0 < ns; c0 += CH) {
+        f32x4_t v[CH];
+        float l[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bool in = c0 + c < ns;
+            v[c] = in ? *(const f32x4_t *)(po + (c0 + c) * po_stride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (SOFTMAX) l[c] = in ? pl[(c0 + c) * split_stride] : -INFINITY;
+        }
+        if constexpr (!SOFTMAX) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) acc += v[c];
         } else {
-            float sum = 0.f;
-            for (int c = 0; c < p.num_splits; ++c) sum += expf(p.part_lse[c * split_stride + rh] - mx);
-            lse = mx + logf(sum);
-            for (int c = 0; c < p.num_splits; ++c) {
-                const float lc = p.part_lse[c * split_stride + rh];
-                if (lc == -INFINITY) continue;
-                acc += expf(lc - lse) * *(const f32x4_t *)(p.part_o + (c * split_stride + rh) * D + chunk * 4);
+            float cm = m;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) cm = fmaxf(cm, l[c]);
+            if (cm == -INFINITY) continue;  // no split of this chunk (or before) saw a key
+            // rescale what was accumulated against the new maximum (m = -inf: factor 0)
+            const float r = __builtin_amdgcn_exp2f((m - cm) * kLog2e);
+            sum *= r;
+            acc *= r;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                // a split that saw nothing has lse_c = -inf and an all-zero partial row
+                const float wc = __builtin_amdgcn_exp2f((l[c] - cm) * kLog2e);
+                sum += wc;
+                acc += wc * v[c];
             }
+            m = cm;
+        }
+    }
+    float lse = 0.f;
+    if constexpr (SOFTMAX) {
+        if (m == -INFINITY) {
+            lse = -INFINITY;  // acc stayed 0
+        } else {
+            acc *= __builtin_amdgcn_rcpf(sum);
+            lse = m + __builtin_amdgcn_logf(sum) * kLn2;  // v_log_f32 is log2
         }
     }
     const int64_t grow = rh / p.H;
