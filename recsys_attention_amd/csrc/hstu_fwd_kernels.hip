@@ -233,6 +233,20 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint8_t *addr) {
 __device__ __forceinline__ void wait_all_loads() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every global->LDS load of this wave landed
 }
+// The same wait at a fixed place in the instruction stream.  The compiler does
+// not see the global->LDS loads, so it treats a vmcnt wait written with the
+// builtin as free to merge into an earlier wait (it has moved the one closing a
+// tile to before the tile's last eight MFMAs, serialising the next tile's load
+// latency into the tile); as a fenced inline-assembly statement it stays where
+// it is written.  (The prologue keeps the builtin: that one also tells the
+// compiler that its own Q loads have completed.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void wait_all_loads_here() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+#pragma clang diagnostic pop
 
 // SiLU of one score without the factor alpha (see silu_block), unmasked.
 __device__ __forceinline__ float silu_raw(float v, float neg_alpha_log2e) {
@@ -412,7 +426,10 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     for (int n = 0; n < ntiles; ++n) {
         const int buf = n & 1;
         const bool has_next = n + 1 < ntiles;
-        const int t_next = bp.tiles.at(has_next ? n + 1 : n);
+        // after the last tile the loads fall past the sequence's buffer range: they
+        // return zeros into the free stage without touching memory, so no load
+        // needs a branch
+        const int t_next = has_next ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
         const int j0 = bp.tiles.at(n) * BN;
         const int32_t st = tile_state(span, j0, j0 + BN);
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
@@ -422,15 +439,15 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             if (wave_any && !wave_mask) {
                 silu_tile_pipelined<E, D>(lds0 + buf * (2 * C::TILE_BYTES), k_addr, v_addr, qreg, oacc,
                                           neg_alpha_log2e, [&](int idx) {
-                                              if (has_next && idx < 2 * C::LOADS)
+                                              if (idx < 2 * C::LOADS)
                                                   issue_one(t_next, buf ^ 1, idx);
                                           });
-                wait_all_loads();
+                wait_all_loads_here();
                 __syncthreads();
                 continue;
             }
         }
-        if (has_next) issue_loads(t_next, buf ^ 1);
+        issue_loads(t_next, buf ^ 1);
         if (wave_any) {
             const uint8_t *stage = lds0 + buf * (2 * C::TILE_BYTES);
             // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             }
         }
 
-        wait_all_loads();
+        wait_all_loads_here();
         __syncthreads();
     }
 
