@@ -292,6 +292,11 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     u32x4_t op0[8], op1[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) op0[kk] = kread(0, kk);
+    // Phases A-C run at wave priority 1 and the MFMA-only phase D at 0, so the
+    // SIMD's other wave (another work-group, usually in a different phase) is
+    // issued ahead of a wave that only feeds the matrix pipe (measured: about
+    // 2 % on the long causal workload).
+    __builtin_amdgcn_s_setprio(1);
     // A (also issues the next tile's eight global->LDS loads, one per step)
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -321,6 +326,7 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     }
     const u32x4_t p1[2] = {pack8(s1, 0), pack8(s1, 8)};
     // D
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) oacc[i & 3] = E::mfma(op1[i], p1[i >> 2], oacc[i & 3]);
 }

@@ -139,12 +139,22 @@ def test_splitkv_matches_unsplit(softmax):
 
 
 def test_schedules_agree_bitwise():
+    """The work order moves work-groups, never the arithmetic of a row."""
     w = W.config("jagged_silu_bf16_d128_local")
     dev = DeviceInputs(w)
     a = dev.forward(schedule=1)
-    b = dev.forward(schedule=2)
+    for sched in (2,):
+        b = dev.forward(schedule=sched)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), sched
+        assert dev.count_pairs(schedule=sched) == dev.count_pairs(schedule=1)
+    w2 = W.random_workload(11, softmax=True, hdim_qk=128, batch=3, nhead=2, max_uih=700,
+                           groups=[W.MaskGroup(0, 6, 0, 0.0)])
+    dev2 = DeviceInputs(w2)
+    r1 = dev2.forward(num_splits=5, schedule=1)
+    r3 = dev2.forward(num_splits=5, schedule=2)
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    assert torch.equal(r1[0], r3[0]) and torch.equal(r1[1], r3[1])
 
 
 def test_jagged_equal_lengths_equals_batched():
