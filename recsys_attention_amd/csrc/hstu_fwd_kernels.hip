@@ -456,6 +456,9 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         issue_loads(t_next, buf ^ 1);
         if (wave_any) {
             const uint8_t *stage = lds0 + buf * (2 * C::TILE_BYTES);
+            // scores and non-linearity at wave priority 1, P.V at 0 (as in the
+            // pipelined tile)
+            __builtin_amdgcn_s_setprio(1);
             // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
             f32x16_t sacc[C::NKB];
 #pragma unroll
@@ -516,6 +519,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 l_run += lsum;
             }
 
+            __builtin_amdgcn_s_setprio(0);
             // ---- O^T += V^T P^T; MFMA step (kb, t2) covers keys
             //      32kb + 16t2 + {4g..4g+3, 8+4g..8+4g+3} in both operands
 #pragma unroll

@@ -116,6 +116,30 @@ def test_random_small_softmax(seed):
 
 
 @pytest.mark.parametrize("seed", range(4))
+def test_random_fp16_silu(seed):
+    """fp16 SiLU at every head dim, jagged and batched (the d128 case runs the
+    pipelined tile body)."""
+    d = (64, 128, 256, 128)[seed]
+    w = W.random_workload(400 + seed, dtype="fp16", hdim_qk=d, jagged=seed != 1, max_uih=500)
+    _check_full(w)
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_groups_with_splitkv(softmax):
+    """Group HSTU (per-group window, context, min-full tail and scale) through the
+    split-KV path, against the oracle.  The scales stay in the operator's regime
+    (the default 1/max UIH length, or 1/256): with attn_scale near 1 a long SiLU
+    row is a small difference of terms summing to ~100 in magnitude, and the bf16
+    rounding of P alone then moves it by more than the absolute bound (a CPU
+    emulation of the kernel's arithmetic reproduces such a GPU value exactly)."""
+    groups = [W.MaskGroup(3, 4, 2, 0.0), W.MaskGroup(0, 6, 0, 1.0 / 256), W.MaskGroup(40, 0, 9, 0.0)]
+    w = W.build("groups_split", dtype="bf16", batch=6, nhead=2, hdim_qk=128, hdim_v=128, jagged=True,
+                cross=False, causal=True, softmax=softmax, alpha=0.0, groups=groups,
+                uih_q=[300, 17, 640, 0, 255, 129], targets=[3, 0, 12, 5, 1, 30], seed=17)
+    _check_full(w, num_splits=4)
+
+
+@pytest.mark.parametrize("seed", range(4))
 def test_random_non_causal(seed):
     w = W.random_workload(300 + seed, causal=False, softmax=bool(seed % 2), hdim_qk=128,
                           max_uih=150)
