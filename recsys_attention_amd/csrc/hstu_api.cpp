@@ -79,8 +79,9 @@ hstu_status_t validate(const hstu_fwd_args_t *a) {
                         (long long)strides[i], (long long)mins[i]);
     }
     {
-        // the kernels address one (sequence, head) through 32-bit byte offsets
-        const int64_t sq = (int64_t)a->seqlen_q, skv = a->cross ? (int64_t)a->seqlen_kv : sq;
+        // the kernels address one (sequence, head) through 32-bit byte offsets,
+        // including up to two key tiles (<= 256 rows) past its end
+        const int64_t sq = (int64_t)a->seqlen_q + 512, skv = (a->cross ? (int64_t)a->seqlen_kv : (int64_t)a->seqlen_q) + 512;
         const int64_t qs = strides[0] ? strides[0] : mins[0], ks = strides[1] ? strides[1] : mins[1],
                       vs = strides[2] ? strides[2] : mins[2];
         if (sq * qs * 2 >= ((int64_t)1 << 32) || skv * ks * 2 >= ((int64_t)1 << 32) ||

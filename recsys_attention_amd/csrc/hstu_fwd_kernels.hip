@@ -372,27 +372,32 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     // ---- global -> LDS loads of key tile t into stage b.  Wave-load c of wave w
     //      fills physical chunks [(4c + w) 64, +64); the chunk a lane lands on
     //      decides which logical chunk (swizzle undone) it fetches.
-    uint32_t ld_row[C::LOADS], ld_kchunk[C::LOADS], ld_vchunk[C::LOADS];
+    //      Physical chunk (c NT + tid) is row c RPC + tid / CPR, chunk tid % CPR; the
+    //      lane's byte offset is its row's offset plus the swizzled chunk, and the
+    //      part that grows with c and with the tile is uniform (it goes into the
+    //      scalar part of the address).  When RPC is a multiple of the swizzle
+    //      period the per-lane parts of all c coincide (one register each).
+    constexpr int RPC = C::NT / C::CPR;
+    const int row0 = tid / C::CPR, pc = tid % C::CPR;
+    uint32_t k_lane[C::LOADS], v_lane[C::LOADS];
 #pragma unroll
     for (int c = 0; c < C::LOADS; ++c) {
-        const int phys = (c * NW + wave) * 64 + lane;
-        const int row = phys / C::CPR, pc = phys % C::CPR;
-        ld_row[c] = (uint32_t)row;
-        ld_kchunk[c] = (uint32_t)(pc ^ (row & kKSwz)) * 16;
-        ld_vchunk[c] = (uint32_t)(pc ^ (kVSwz * (row & 3))) * 16;
+        const int rsw = (RPC & kKSwz) == 0 ? row0 : c * RPC + row0;
+        k_lane[c] = (uint32_t)row0 * ks2 + (uint32_t)(pc ^ (rsw & kKSwz)) * 16;
+        v_lane[c] = (uint32_t)row0 * vs2 + (uint32_t)(pc ^ (kVSwz * (row0 & 3))) * 16;
     }
     // LDS byte address of this wave's first landing slot (wave-uniform)
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] +
                               (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024;
     // load idx of key tile t into stage b: idx < LOADS are K chunks, the rest V
     auto issue_one = [&](int t, int b, int idx) {
-        const uint32_t j0 = (uint32_t)(t * BN);
         const int c = idx % C::LOADS;
+        const uint32_t r = (uint32_t)(t * BN + c * RPC);  // uniform
         const uint32_t dst = lds_base + b * (2 * C::TILE_BYTES) + c * NW * 1024;
         if (idx < C::LOADS)
-            load_to_lds(kr, dst, (j0 + ld_row[c]) * ks2 + ld_kchunk[c]);
+            load_to_lds(kr, dst, k_lane[c] + r * ks2);
         else
-            load_to_lds(vr, dst + C::TILE_BYTES, (j0 + ld_row[c]) * vs2 + ld_vchunk[c]);
+            load_to_lds(vr, dst + C::TILE_BYTES, v_lane[c] + r * vs2);
     };
     auto issue_loads = [&](int t, int b) {
 #pragma unroll
