@@ -84,8 +84,8 @@ typedef struct {
     int32_t dtype;     /* hstu_dtype_t of q, k, v and o */
     int32_t batch;     /* number of sequences B (>= 0) */
     int32_t nhead;     /* heads H (>= 1) */
-    int32_t hdim_qk;   /* 64, 128 or 256 */
-    int32_t hdim_v;    /* equal to hdim_qk in this build */
+    int32_t hdim_qk;   /* (hdim_qk, hdim_v) in {64/64, 96/96, 96/64, 128/128, 256/256} */
+    int32_t hdim_v;    /* other pairs: HSTU_ERR_UNSUPPORTED */
     int32_t jagged;    /* 0: batched [B, S, H, D]; 1: jagged [1, total, H, D] + seq_offsets */
     int32_t cross;     /* 0: self-attention (k/v laid out like q, targets included); 1: cross */
     int32_t seqlen_q;  /* batched: physical S_q; jagged: an upper bound of every S_q (grid size) */

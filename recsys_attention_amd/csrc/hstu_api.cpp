@@ -38,9 +38,13 @@ hstu_status_t validate(const hstu_fwd_args_t *a) {
     if (a->nhead < 1) return fail(HSTU_ERR_INVALID_ARG, "nhead %d < 1", a->nhead);
     if (a->hdim_qk <= 0 || a->hdim_v <= 0)
         return fail(HSTU_ERR_INVALID_ARG, "head dims must be positive (%d, %d)", a->hdim_qk, a->hdim_v);
-    if (a->hdim_qk != a->hdim_v || (a->hdim_qk != 64 && a->hdim_qk != 128 && a->hdim_qk != 256))
-        return fail(HSTU_ERR_UNSUPPORTED, "head dims (%d, %d): built for 64/64, 128/128, 256/256",
-                    a->hdim_qk, a->hdim_v);
+    {
+        const int dq = a->hdim_qk, dv = a->hdim_v;
+        const bool built = (dq == dv && (dq == 64 || dq == 96 || dq == 128 || dq == 256)) || (dq == 96 && dv == 64);
+        if (!built)
+            return fail(HSTU_ERR_UNSUPPORTED,
+                        "head dims (%d, %d): built for 64/64, 96/96, 96/64, 128/128, 256/256", dq, dv);
+    }
     for (int32_t f : {a->jagged, a->cross, a->causal, a->softmax})
         if (f != 0 && f != 1) return fail(HSTU_ERR_INVALID_ARG, "jagged/cross/causal/softmax must be 0 or 1");
     if (a->schedule < 0 || a->schedule > 2)
@@ -189,7 +193,7 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
     fill_params(args, 1, p);
     if ((st = check_grid(p)) != HSTU_OK) return st;
     if (p.total_rows == 0 || p.B == 0) return HSTU_OK;
-    return hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->softmax != 0, false,
+    return hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, false,
                                            (hipStream_t)hip_stream),
                       "forward kernel launch");
 }
@@ -215,7 +219,7 @@ hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, 
     p.part_lse = args->softmax ? (float *)((char *)ws + ((rows * args->hdim_v * sizeof(float) + 255) / 256) * 256)
                                : nullptr;
     hipStream_t stream = (hipStream_t)hip_stream;
-    st = hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->softmax != 0, true, stream),
+    st = hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, true, stream),
                     "split-KV kernel launch");
     if (st != HSTU_OK) return st;
     return hip_status(hstu::launch_combine(p, args->dtype, args->hdim_v, args->softmax != 0, stream),

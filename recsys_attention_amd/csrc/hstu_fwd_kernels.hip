@@ -76,19 +76,23 @@ struct Elem<HSTU_FP16> {
 // device): K chunk c of row r is stored at chunk c ^ (r & 15) (the 32 lanes of
 // a half-wave read one chunk of 32 consecutive rows), V chunk c at c ^ 4(r & 3)
 // (the transposed reads touch four consecutive rows, 64 bytes each).
-template <int D, int BN, int NW = 4>
+template <int D, int BN, int NW = 4, int DV = D>
 struct Tile {
     static constexpr int BM = 32 * NW;       // query rows per work-group (32 per wave)
     static constexpr int NT = 64 * NW;       // threads
-    static constexpr int RB = D * 2;         // bytes per K or V row
-    static constexpr int CPR = D / 8;        // 16-byte chunks per row
-    static constexpr int TILE_BYTES = BN * RB;
+    static constexpr int RB = D * 2;         // bytes per K row (hdim_qk = D)
+    static constexpr int CPR = D / 8;        // 16-byte chunks per K row
+    static constexpr int TILE_BYTES = BN * RB;   // K tile
+    static constexpr int RBV = DV * 2;       // bytes per V row (hdim_v = DV)
+    static constexpr int CPRV = DV / 8;
+    static constexpr int TILE_V = BN * RBV;
+    static constexpr int STAGE = TILE_BYTES + TILE_V;  // one ring stage: [K tile | V tile]
     static constexpr int KSTEPS = D / 16;    // MFMA k-steps of Q.K^T
     static constexpr int NKB = BN / 32;      // 32-key blocks per tile
-    static constexpr int NDB = D / 32;       // 32-column blocks of the output
-    static constexpr int LOADS = BN * CPR / NT;  // 16-byte chunks each thread loads per tensor
-    static_assert(LOADS * NT == BN * CPR, "the loads cover the tile exactly");
-    static_assert(64 % CPR == 0, "one wave-load covers whole rows");
+    static constexpr int NDB = DV / 32;      // 32-column blocks of the output
+    static constexpr int LOADS = BN * CPR / NT;     // 16-byte chunks each thread loads of K
+    static constexpr int LOADS_V = BN * CPRV / NT;  // and of V
+    static_assert(LOADS * NT == BN * CPR && LOADS_V * NT == BN * CPRV, "the loads cover the tiles exactly");
 };
 
 __device__ __forceinline__ int32_t wave_min(int32_t x) {
@@ -331,18 +335,19 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     for (int i = 0; i < 8; ++i) oacc[i & 3] = E::mfma(op1[i], p1[i >> 2], oacc[i & 3]);
 }
 
-template <int DT, int D, bool SOFTMAX, bool SPLIT>
+template <int DT, int D, bool SOFTMAX, bool SPLIT, int DV = D>
 __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
     constexpr int NW = waves_for(D);
-    using C = Tile<D, BN, NW>;
+    using C = Tile<D, BN, NW, DV>;
     // K swizzle over the low 4 chunk bits (3 when a row has only 8 chunks);
-    // V swizzle 4(r & 3) needs 16 chunks per row, 2(r & 3) with 8
-    constexpr int kKSwz = C::CPR >= 16 ? 15 : 7;
-    constexpr int kVSwz = C::CPR >= 16 ? 4 : 2;
+    // V swizzle 4(r & 3) needs 16 chunks per row, 2(r & 3) with 8.  Rows of 12
+    // chunks (hdim 96) are not swizzled (an XOR would leave the row).
+    constexpr int kKSwz = C::CPR >= 16 ? 15 : (C::CPR == 8 ? 7 : 0);
+    constexpr int kVSwz = C::CPRV >= 16 ? 4 : (C::CPRV == 8 ? 2 : 0);
     using E = Elem<DT>;
     // two stages of [K tile | V tile]
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][C::STAGE];
     __shared__ int32_t red[2 * NW];
 
     BlockPlan bp;
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     const i32x4_t kr =
         make_rsrc_words((const uint16_t *)p.k + s.kv0 * p.k_stride + h * D, (uint32_t)s.S_kv * ks2);
     const i32x4_t vr =
-        make_rsrc_words((const uint16_t *)p.v + s.kv0 * p.v_stride + h * D, (uint32_t)s.S_kv * vs2);
+        make_rsrc_words((const uint16_t *)p.v + s.kv0 * p.v_stride + h * DV, (uint32_t)s.S_kv * vs2);
 
     // ---- Q^T operand: lane holds d = 16*kk + 8*g .. +7 of its row
     u32x4_t qreg[C::KSTEPS];
@@ -372,43 +377,54 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     // ---- global -> LDS loads of key tile t into stage b.  Wave-load c of wave w
     //      fills physical chunks [(4c + w) 64, +64); the chunk a lane lands on
     //      decides which logical chunk (swizzle undone) it fetches.
-    //      Physical chunk (c NT + tid) is row c RPC + tid / CPR, chunk tid % CPR; the
-    //      lane's byte offset is its row's offset plus the swizzled chunk, and the
-    //      part that grows with c and with the tile is uniform (it goes into the
-    //      scalar part of the address).  When RPC is a multiple of the swizzle
-    //      period the per-lane parts of all c coincide (one register each).
-    constexpr int RPC = C::NT / C::CPR;
-    const int row0 = tid / C::CPR, pc = tid % C::CPR;
-    uint32_t k_lane[C::LOADS], v_lane[C::LOADS];
+    //      Physical chunk (c NT + tid) is row (c NT + tid) / CPR, chunk (c NT + tid) %
+    //      CPR; the lane's byte offset is its row's offset plus the swizzled chunk.
+    //      With whole rows per wave-load (CPR divides NT) the part that grows with c
+    //      is uniform (it goes with the tile into the scalar part of the address),
+    //      and when RPC is a multiple of the swizzle period the per-lane parts of all
+    //      c coincide (one register each).
+    constexpr bool kRowsK = C::NT % C::CPR == 0, kRowsV = C::NT % C::CPRV == 0;
+    constexpr int RPC = kRowsK ? C::NT / C::CPR : 0, RPCV = kRowsV ? C::NT / C::CPRV : 0;
+    uint32_t k_lane[C::LOADS], v_lane[C::LOADS_V];
 #pragma unroll
     for (int c = 0; c < C::LOADS; ++c) {
-        const int rsw = (RPC & kKSwz) == 0 ? row0 : c * RPC + row0;
-        k_lane[c] = (uint32_t)row0 * ks2 + (uint32_t)(pc ^ (rsw & kKSwz)) * 16;
-        v_lane[c] = (uint32_t)row0 * vs2 + (uint32_t)(pc ^ (kVSwz * (row0 & 3))) * 16;
+        const int phys = kRowsK ? tid : c * C::NT + tid;
+        const int row = phys / C::CPR, pc = phys % C::CPR;
+        const int rsw = (RPC & kKSwz) == 0 ? row : c * RPC + row;
+        k_lane[c] = (uint32_t)row * ks2 + (uint32_t)(pc ^ (rsw & kKSwz)) * 16;
+    }
+#pragma unroll
+    for (int c = 0; c < C::LOADS_V; ++c) {
+        const int phys = kRowsV ? tid : c * C::NT + tid;
+        const int row = phys / C::CPRV, pc = phys % C::CPRV;
+        v_lane[c] = (uint32_t)row * vs2 + (uint32_t)(pc ^ (kVSwz * (row & 3))) * 16;
     }
     // LDS byte address of this wave's first landing slot (wave-uniform)
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] +
                               (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024;
     // load idx of key tile t into stage b: idx < LOADS are K chunks, the rest V
+    constexpr int LPT = C::LOADS + C::LOADS_V;  // loads per tile and wave
     auto issue_one = [&](int t, int b, int idx) {
-        const int c = idx % C::LOADS;
-        const uint32_t r = (uint32_t)(t * BN + c * RPC);  // uniform
-        const uint32_t dst = lds_base + b * (2 * C::TILE_BYTES) + c * NW * 1024;
-        if (idx < C::LOADS)
-            load_to_lds(kr, dst, k_lane[c] + r * ks2);
-        else
-            load_to_lds(vr, dst + C::TILE_BYTES, v_lane[c] + r * vs2);
+        if (idx < C::LOADS) {
+            const int c = idx;
+            const uint32_t r = (uint32_t)(t * BN + c * RPC);  // uniform
+            load_to_lds(kr, lds_base + b * C::STAGE + c * NW * 1024, k_lane[c] + r * ks2);
+        } else {
+            const int c = idx - C::LOADS;
+            const uint32_t r = (uint32_t)(t * BN + c * RPCV);
+            load_to_lds(vr, lds_base + b * C::STAGE + C::TILE_BYTES + c * NW * 1024, v_lane[c] + r * vs2);
+        }
     };
     auto issue_loads = [&](int t, int b) {
 #pragma unroll
-        for (int idx = 0; idx < 2 * C::LOADS; ++idx) issue_one(t, b, idx);
+        for (int idx = 0; idx < LPT; ++idx) issue_one(t, b, idx);
     };
 
     // ---- per-lane LDS read addresses (stage 0; stage 1 adds 2 * TILE_BYTES)
     // K operand of S^T = K Q^T: row 32kb + r32, logical chunk 2kk + g
     // (the swizzle mixes the low log2(NKA)+1 chunk bits, so NKA k-steps get their own
     //  lane offsets and later k-steps repeat them one swizzle period further on)
-    constexpr int NKA = (kKSwz + 1) / 2, NVA = kVSwz == 4 ? 4 : 2;
+    constexpr int NKA = kKSwz ? (kKSwz + 1) / 2 : 1, NVA = kVSwz == 4 ? 4 : (kVSwz == 2 ? 2 : 1);
     uint32_t k_addr[NKA];
 #pragma unroll
     for (int m = 0; m < NKA; ++m)
@@ -419,7 +435,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     uint32_t v_addr[NVA];
 #pragma unroll
     for (int b2 = 0; b2 < NVA; ++b2)
-        v_addr[b2] = (uint32_t)(C::TILE_BYTES + (4 * g + (i16 >> 2)) * C::RB +
+        v_addr[b2] = (uint32_t)(C::TILE_BYTES + (4 * g + (i16 >> 2)) * C::RBV +
                                 (((4 * b2 + 2 * hb + ((i16 & 3) >> 1)) ^ vy) * 16) + (i16 & 1) * 8);
 
     f32x16_t oacc[C::NDB];
@@ -446,12 +462,11 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
         const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
 
-        if constexpr (!SOFTMAX && D == 128) {
+        if constexpr (!SOFTMAX && D == 128 && DV == 128) {
             if (wave_any && !wave_mask) {
-                silu_tile_pipelined<E, D>(lds0 + buf * (2 * C::TILE_BYTES), k_addr, v_addr, qreg, oacc,
+                silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc,
                                           neg_alpha_log2e, [&](int idx) {
-                                              if (idx < 2 * C::LOADS)
-                                                  issue_one(t_next, buf ^ 1, idx);
+                                              if (idx < LPT) issue_one(t_next, buf ^ 1, idx);
                                           });
                 wait_all_loads_here();
                 __syncthreads();
@@ -460,7 +475,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         }
         issue_loads(t_next, buf ^ 1);
         if (wave_any) {
-            const uint8_t *stage = lds0 + buf * (2 * C::TILE_BYTES);
+            const uint8_t *stage = lds0 + buf * C::STAGE;
             // scores and non-linearity at wave priority 1, P.V at 0 (as in the
             // pipelined tile)
             __builtin_amdgcn_s_setprio(1);
@@ -539,9 +554,9 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                     const int key0 = kb * 32 + 16 * t2;
 #pragma unroll
                     for (int nb = 0; nb < C::NDB; ++nb) {
-                        const uint8_t *va = stage + v_addr[nb % NVA] + key0 * C::RB + (nb / NVA) * (NVA * 64);
+                        const uint8_t *va = stage + v_addr[nb % NVA] + key0 * C::RBV + (nb / NVA) * (NVA * 64);
                         const u32x2_t a0 = lds_read_tr16(va);
-                        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RB);
+                        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RBV);
                         oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb, oacc[nb]);
                     }
                 }
@@ -563,7 +578,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     if (!span.valid) return;
     const int64_t grow = s.q0 + bp.row;  // token row of o
     if constexpr (!SPLIT) {
-        uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * D + 4 * g;
+        uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * DV + 4 * g;
 #pragma unroll
         for (int nb = 0; nb < C::NDB; ++nb) {
 #pragma unroll
@@ -585,7 +600,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         // fp32 partials, already multiplied by attn_scale (softmax: normalised
         // by this split's own sum; the combine pass reweights by the LSEs)
         const int64_t prow = ((int64_t)bp.it.sp * p.total_rows + grow) * p.H + h;
-        float *pp = p.part_o + prow * D + 4 * g;
+        float *pp = p.part_o + prow * DV + 4 * g;
 #pragma unroll
         for (int nb = 0; nb < C::NDB; ++nb) {
 #pragma unroll
@@ -719,35 +734,36 @@ __global__ void hstu_zero_u64(unsigned long long *x) { *x = 0; }
 
 // ------------------------------------------------------------------ launchers
 
-template <int DT, int D, bool SOFTMAX, bool SPLIT>
+template <int DT, int D, int DV, bool SOFTMAX, bool SPLIT>
 static hipError_t launch_one(const KernelParams &p, hipStream_t stream) {
     const int64_t grid = grid_size(p);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT>), dim3((unsigned)grid), dim3(64 * waves_for(D)), 0,
-                       stream, p);
+    hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV>), dim3((unsigned)grid), dim3(64 * waves_for(D)),
+                       0, stream, p);
     return hipGetLastError();
 }
 
-template <int DT, int D>
+template <int DT, int D, int DV>
 static hipError_t launch_d(const KernelParams &p, bool softmax, bool split, hipStream_t stream) {
-    if (softmax) return split ? launch_one<DT, D, true, true>(p, stream) : launch_one<DT, D, true, false>(p, stream);
-    return split ? launch_one<DT, D, false, true>(p, stream) : launch_one<DT, D, false, false>(p, stream);
+    if (softmax)
+        return split ? launch_one<DT, D, DV, true, true>(p, stream) : launch_one<DT, D, DV, true, false>(p, stream);
+    return split ? launch_one<DT, D, DV, false, true>(p, stream) : launch_one<DT, D, DV, false, false>(p, stream);
 }
 
 template <int DT>
-static hipError_t launch_dt(const KernelParams &p, int D, bool softmax, bool split, hipStream_t stream) {
-    switch (D) {
-        case 64: return launch_d<DT, 64>(p, softmax, split, stream);
-        case 128: return launch_d<DT, 128>(p, softmax, split, stream);
-        case 256: return launch_d<DT, 256>(p, softmax, split, stream);
-        default: return hipErrorInvalidValue;
-    }
+static hipError_t launch_dt(const KernelParams &p, int D, int DV, bool softmax, bool split, hipStream_t stream) {
+    if (D == 64 && DV == 64) return launch_d<DT, 64, 64>(p, softmax, split, stream);
+    if (D == 96 && DV == 96) return launch_d<DT, 96, 96>(p, softmax, split, stream);
+    if (D == 96 && DV == 64) return launch_d<DT, 96, 64>(p, softmax, split, stream);
+    if (D == 128 && DV == 128) return launch_d<DT, 128, 128>(p, softmax, split, stream);
+    if (D == 256 && DV == 256) return launch_d<DT, 256, 256>(p, softmax, split, stream);
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_forward(const KernelParams &p, int dtype, int D, bool softmax, bool split,
+hipError_t launch_forward(const KernelParams &p, int dtype, int D, int DV, bool softmax, bool split,
                           hipStream_t stream) {
-    return dtype == HSTU_BF16 ? launch_dt<HSTU_BF16>(p, D, softmax, split, stream)
-                              : launch_dt<HSTU_FP16>(p, D, softmax, split, stream);
+    return dtype == HSTU_BF16 ? launch_dt<HSTU_BF16>(p, D, DV, softmax, split, stream)
+                              : launch_dt<HSTU_FP16>(p, D, DV, softmax, split, stream);
 }
 
 hipError_t launch_combine(const KernelParams &p, int dtype, int D, bool softmax, hipStream_t stream) {
@@ -774,6 +790,7 @@ hipError_t launch_count(const KernelParams &p, int D, unsigned long long *count,
     if (grid > 0) {
         switch (D) {
             case 64: hipLaunchKernelGGL((hstu_count_kernel<key_tile_for(64), waves_for(64)>), dim3((unsigned)grid), dim3(64 * waves_for(64)), 0, stream, p, count); break;
+            case 96: hipLaunchKernelGGL((hstu_count_kernel<key_tile_for(96), waves_for(96)>), dim3((unsigned)grid), dim3(64 * waves_for(96)), 0, stream, p, count); break;
             case 128: hipLaunchKernelGGL((hstu_count_kernel<key_tile_for(128), waves_for(128)>), dim3((unsigned)grid), dim3(64 * waves_for(128)), 0, stream, p, count); break;
             case 256: hipLaunchKernelGGL((hstu_count_kernel<key_tile_for(256), waves_for(256)>), dim3((unsigned)grid), dim3(64 * waves_for(256)), 0, stream, p, count); break;
             default: return hipErrorInvalidValue;

@@ -9,14 +9,14 @@ namespace hstu {
 
 // The kernels' tiling per head dim: key-tile width, waves per work-group (32
 // query rows each) and so query rows per work-group.
-constexpr int key_tile_for(int D) { return D == 64 ? 128 : (D == 128 ? 64 : 32); }
+constexpr int key_tile_for(int D) { return D <= 64 ? 128 : (D <= 128 ? 64 : 32); }
 // Four waves (128 rows): two work-groups then share a CU; eight-wave work-groups
 // (one per CU) halve the key/value traffic into LDS per row but measured slower,
 // since the CU-wide barrier keeps the two waves of each SIMD in the same phase.
 constexpr int waves_for(int) { return 4; }
 constexpr int block_m_for(int D) { return 32 * waves_for(D); }
 
-hipError_t launch_forward(const KernelParams &p, int dtype, int D, bool softmax, bool split,
+hipError_t launch_forward(const KernelParams &p, int dtype, int D, int DV, bool softmax, bool split,
                           hipStream_t stream);
 hipError_t launch_combine(const KernelParams &p, int dtype, int D, bool softmax, hipStream_t stream);
 hipError_t launch_count(const KernelParams &p, int D, unsigned long long *count, hipStream_t stream);

@@ -63,7 +63,8 @@ def test_valid_args_pass(lib):
     (dict(dtype=7), _abi.HSTU_ERR_INVALID_ARG),
     (dict(batch=-1), _abi.HSTU_ERR_INVALID_ARG),
     (dict(nhead=0), _abi.HSTU_ERR_INVALID_ARG),
-    (dict(hdim_qk=96, hdim_v=64), _abi.HSTU_ERR_UNSUPPORTED),
+    (dict(hdim_qk=96, hdim_v=128), _abi.HSTU_ERR_UNSUPPORTED),
+    (dict(hdim_qk=80, hdim_v=80), _abi.HSTU_ERR_UNSUPPORTED),
     (dict(hdim_qk=32, hdim_v=32), _abi.HSTU_ERR_UNSUPPORTED),
     (dict(seq_offsets_q=None), _abi.HSTU_ERR_INVALID_ARG),
     (dict(cross=1), _abi.HSTU_ERR_INVALID_ARG),            # jagged cross without kv offsets

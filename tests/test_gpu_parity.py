@@ -139,6 +139,21 @@ def test_groups_with_splitkv(softmax):
     _check_full(w, num_splits=4)
 
 
+@pytest.mark.parametrize("dims", [(96, 96), (96, 64)])
+@pytest.mark.parametrize("softmax", [False, True])
+def test_hdim96(dims, softmax):
+    """Head dims 96/96 and 96/64 (rows of 12 16-byte chunks, V narrower than Q/K):
+    jagged self-attention with every mask component, then cross-attention through
+    split-KV."""
+    dqk, dv = dims
+    w = W.random_workload(500 + dqk + dv + softmax, hdim_qk=dqk, hdim_v=dv, softmax=softmax,
+                          max_uih=400)
+    _check_full(w)
+    w = W.random_workload(600 + dqk + dv + softmax, dtype="fp16", hdim_qk=dqk, hdim_v=dv,
+                          softmax=softmax, cross=True, max_uih=300)
+    _check_full(w, num_splits=3)
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_random_non_causal(seed):
     w = W.random_workload(300 + seed, causal=False, softmax=bool(seed % 2), hdim_qk=128,

@@ -95,21 +95,22 @@ def test_default_alpha_is_inverse_sqrt_hdim():
     assert np.array_equal(o0, o1)
 
 
-@pytest.mark.parametrize("L", [0, 4])
-def test_silu_equals_dense_masked_product(L):
-    """No context/targets: o = a * (band ⊙ SiLU(alpha Q K^T)) V with torch's silu."""
+@pytest.mark.parametrize("L,Dv", [(0, 32), (4, 32), (4, 48)])
+def test_silu_equals_dense_masked_product(L, Dv):
+    """No context/targets: o = a * (band ⊙ SiLU(alpha Q K^T)) V with torch's silu
+    (also with a value head dim different from the query/key one)."""
     B, H, D, S = 2, 2, 32, 29
-    q, k, v = _rand((B * S, H, D), 7), _rand((B * S, H, D), 8), _rand((B * S, H, D), 9)
+    q, k, v = _rand((B * S, H, D), 7), _rand((B * S, H, D), 8), _rand((B * S, H, Dv), 9)
     alpha, a = 0.4, 0.05
-    o, _, pairs = oracle.forward(_problem(B, H, D, S, L=L, alpha=alpha, a=a), q, k, v)
+    o, _, pairs = oracle.forward(_problem(B, H, D, S, L=L, alpha=alpha, a=a, Dv=Dv), q, k, v)
     tq = torch.from_numpy(q).double().view(B, S, H, D).transpose(1, 2)
     tk = torch.from_numpy(k).double().view(B, S, H, D).transpose(1, 2)
-    tv = torch.from_numpy(v).double().view(B, S, H, D).transpose(1, 2)
+    tv = torch.from_numpy(v).double().view(B, S, H, Dv).transpose(1, 2)
     band = torch.ones(S, S, dtype=torch.float64).tril()
     if L:
         band = band - torch.ones(S, S, dtype=torch.float64).tril(-L - 1)
     ref = a * (band * torch.nn.functional.silu(alpha * (tq @ tk.transpose(-1, -2)))) @ tv
-    ref = ref.transpose(1, 2).reshape(B * S, H, D).numpy()
+    ref = ref.transpose(1, 2).reshape(B * S, H, Dv).numpy()
     assert np.abs(o - ref).max() < 1e-12
     assert pairs == B * H * int(band.sum())
 
