@@ -154,6 +154,37 @@ def test_hdim96(dims, softmax):
     _check_full(w, num_splits=3)
 
 
+@pytest.mark.parametrize("softmax", [False, True])
+def test_mfalcon_candidates_against_cached_history(softmax):
+    """M-FALCON-style ranking (explainer "M-FALCON"): a user's history is a cached
+    key/value sequence and the candidates are target queries of a cross-attention
+    call with no query history.  Candidates never attend to each other, so scoring
+    them all at once and in microbatches of 16 against the same cache gives the
+    same rows bit for bit, and the oracle's values."""
+    hist, cands = [700, 130, 1500], [37, 5, 64]
+    groups = [W.MaskGroup(0, 0, 0, 1.0 / 512)]  # no query history to derive the scale from
+    kw = dict(dtype="bf16", nhead=2, hdim_qk=128, hdim_v=128, jagged=True, cross=True, causal=True,
+              softmax=softmax, alpha=0.0, groups=groups)
+    w = W.build("mfalcon", batch=3, uih_q=[0, 0, 0], targets=cands, uih_kv=hist, seed=23, **kw)
+    _check_full(w)
+    res = DeviceInputs(w).forward()
+    o_all = o_tokens(w, res[0] if softmax else res)
+    lse_all = lse_tokens(w, res[1]) if softmax else None
+    for b in range(w.batch):
+        q0, k0, k1 = w.q_offsets[b], w.kv_offsets[b], w.kv_offsets[b + 1]
+        for s0 in range(0, cands[b], 16):
+            e0 = min(cands[b], s0 + 16)
+            sub = W.build("mb", batch=1, uih_q=[0], targets=[e0 - s0], uih_kv=[hist[b]],
+                          materialize=False, **kw)
+            sub.q_bits = w.q_bits[q0 + s0:q0 + e0]
+            sub.k_bits, sub.v_bits = w.k_bits[k0:k1], w.v_bits[k0:k1]
+            r = DeviceInputs(sub).forward()
+            torch.cuda.synchronize()
+            assert np.array_equal(o_tokens(sub, r[0] if softmax else r), o_all[q0 + s0:q0 + e0]), (b, s0)
+            if softmax:
+                assert np.array_equal(lse_tokens(sub, r[1]), lse_all[q0 + s0:q0 + e0]), (b, s0)
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_random_non_causal(seed):
     w = W.random_workload(300 + seed, causal=False, softmax=bool(seed % 2), hdim_qk=128,
