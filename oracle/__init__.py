@@ -16,6 +16,10 @@ Parity status (what pins each function, see tests/test_oracle_*.py):
                     section 3.4) and by the dense causal special case.
   * softmax + LSE - pinned by torch scaled_dot_product_attention in float64
                     (causal and full special cases) and the worked example.
+  * relative attention bias - the time-gap buckets pinned by the explainer's
+                    bucket table (tests/golden/rab_time_buckets.json); the bias
+                    as a whole by SDPA with an additive float mask (softmax) and
+                    the dense SiLU product with the bias added (SiLU).
 """
 from __future__ import annotations
 
@@ -66,10 +70,14 @@ def load(path: Optional[str] = None):
                                                 _i32p, _f64p, _f64p, ctypes.c_int]
     lib.oracle_count_pairs.argtypes = _PROBLEM + [_i64p]
     lib.oracle_seq_info.argtypes = _PROBLEM + [_i32p, _f64p]
+    lib.oracle_hstu_fwd_rab.argtypes = _PROBLEM + [_i32p, _f64p, _f64p, ctypes.c_int, _f32p, _f32p,
+                                                   _f32p, _f64p, _f64p, _i64p, ctypes.c_int]
+    lib.oracle_rab_bucket.argtypes = [ctypes.c_int64]
+    lib.oracle_rab_bucket.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
-    for f in ("oracle_mask", "oracle_hstu_fwd", "oracle_hstu_rows", "oracle_count_pairs",
-              "oracle_seq_info"):
+    for f in ("oracle_mask", "oracle_hstu_fwd", "oracle_hstu_fwd_rab", "oracle_hstu_rows",
+              "oracle_count_pairs", "oracle_seq_info"):
         getattr(lib, f).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -148,6 +156,33 @@ def forward(p: Problem, q, k, v, nthreads: int = 0, lib=None):
     if rc != 0:
         raise ValueError("oracle_hstu_fwd rejected its arguments")
     return o, lse, int(pairs[0])
+
+
+def forward_rab(p: Problem, q, k, v, timestamps=None, time_table=None, pos_table=None,
+                nthreads: int = 0, lib=None):
+    """Whole forward with the relative attention bias (self-attention only).
+    timestamps: int32 [tokens] or None; time_table [H, 11]; pos_table [H, P] or None.
+    Returns (o, lse, pairs) like forward()."""
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    ts = None if timestamps is None else np.ascontiguousarray(timestamps, np.int32)
+    tt = None if time_table is None else np.ascontiguousarray(time_table, np.float64)
+    pt = None if pos_table is None else np.ascontiguousarray(pos_table, np.float64)
+    P = 0 if pt is None else int(pt.shape[1])
+    o = np.zeros((p.total_q, p.H, p.Dv), np.float64)
+    lse = np.zeros((p.total_q, p.H), np.float64) if p.softmax else None
+    pairs = np.zeros(1, np.int64)
+    rc = lib.oracle_hstu_fwd_rab(*p.args(), _ptr(ts, _i32p), _ptr(tt, _f64p), _ptr(pt, _f64p), P,
+                                 _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(o, _f64p),
+                                 _ptr(lse, _f64p), _ptr(pairs, _i64p), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_hstu_fwd_rab rejected its arguments")
+    return o, lse, int(pairs[0])
+
+
+def rab_bucket(d: int, lib=None) -> int:
+    """Time-gap bucket (0..10) of a gap of d seconds."""
+    return int((lib or load()).oracle_rab_bucket(int(d)))
 
 
 def rows(p: Problem, q, k, v, rows_b, rows_h, rows_i, nthreads: int = 0, lib=None):

@@ -39,6 +39,16 @@
  *       before it).
  * Lengths that do not fit (S < C + T) are clamped: C' = min(C, S),
  * T' = min(T, S - C'), U = S - C' - T'.
+ *
+ * Relative attention bias (HSTU explainer, "The layer, line by line" (b) and
+ * "The relative attention bias"; self-attention only), added to the score
+ * before the mask and the non-linearity:
+ *   s[b,h,i,j] = alpha * q_i . k_j + rab_pos[h][min(|i - j|, P - 1)]
+ *                                  + rab_time[h][bucket(|ts_i - ts_j|)]
+ * with i, j the physical positions in the sequence, ts the per-token integer
+ * timestamps (seconds) and bucket(d) the number of the explainer's bucket edges
+ * 1, 5, 30, 60, 300, 1800, 3600, 86400, 604800, 2.6e6 that are <= d (11
+ * buckets, 0 for d < 1, 10 for d >= 2.6e6).  Either term may be absent.
  */
 #include <math.h>
 #include <stdint.h>
@@ -104,10 +114,47 @@ static int visible(const seq_t *s, int i, int j)
     return d <= s->L && d >= -s->L;      /* (6) */
 }
 
+/* relative attention bias tables (NULL members: term absent) */
+typedef struct {
+    const int32_t *ts;        /* [tokens] timestamps of the sequence tokens */
+    const double *time_tab;   /* [H][11] */
+    const double *pos_tab;    /* [H][P] */
+    int P;
+} rab_t;
+
+#define RAB_BUCKETS 11
+/* the explainer's time-gap bucket edges (seconds): 1 s, 5 s, 30 s, 1 min, 5 min,
+ * 30 min, 1 h, 1 d, 1 w, ~1 mo */
+static const int64_t kRabEdges[RAB_BUCKETS - 1] = {1, 5, 30, 60, 300, 1800, 3600, 86400, 604800, 2600000};
+
+int oracle_rab_bucket(int64_t d)
+{
+    if (d < 0) d = -d;
+    int b = 0;
+    for (int e = 0; e < RAB_BUCKETS - 1; ++e)
+        if (kRabEdges[e] <= d) b = e + 1;
+    return b;
+}
+
+static double rab_bias(const rab_t *r, const seq_t *s, int h, int i, int j)
+{
+    double bias = 0.0;
+    if (!r) return bias;
+    if (r->pos_tab) {
+        int d = i > j ? i - j : j - i;
+        bias += r->pos_tab[(int64_t)h * r->P + imin(d, r->P - 1)];
+    }
+    if (r->ts) {
+        int64_t d = (int64_t)r->ts[s->q0 + i] - (int64_t)r->ts[s->kv0 + j];
+        bias += r->time_tab[(int64_t)h * RAB_BUCKETS + oracle_rab_bucket(d)];
+    }
+    return bias;
+}
+
 /* one output row: o_row[Dv] (and *lse) from the row's dense mask */
 static void row_forward(const seq_t *s, int h, int i, const unsigned char *mask_row,
                         int H, int Dqk, int Dv, int softmax, double alpha,
-                        const float *q, const float *k, const float *v,
+                        const float *q, const float *k, const float *v, const rab_t *rab,
                         double *o_row, double *lse_out, double *sbuf)
 {
     const float *qi = q + ((s->q0 + i) * H + h) * (int64_t)Dqk;
@@ -120,7 +167,7 @@ static void row_forward(const seq_t *s, int h, int i, const unsigned char *mask_
         const float *kj = k + ((s->kv0 + j) * H + h) * (int64_t)Dqk;
         double dot = 0.0;
         for (int e = 0; e < Dqk; ++e) dot += (double)qi[e] * (double)kj[e];
-        sbuf[j] = alpha * dot;
+        sbuf[j] = alpha * dot + rab_bias(rab, s, h, i, j);
         if (sbuf[j] > smax) smax = sbuf[j];
         ++nvis;
     }
@@ -227,10 +274,35 @@ int oracle_mask(int S_q, int S_kv, int C, int T, int cross, int L, int M, int ca
 /* Full forward.  q,k: [tokens][H][Dqk] fp32, v: [tokens][H][Dv] fp32.
  * o: [total_q][H][Dv] double; lse (softmax, may be NULL): [total_q][H] double;
  * *pairs (may be NULL): number of visible (b, h, i, j).  nthreads <= 0: default. */
+static int hstu_fwd_impl(const problem_t *pp, const rab_t *rab, const float *q, const float *k,
+                         const float *v, double *o, double *lse, int64_t *pairs, int nthreads);
+
 int oracle_hstu_fwd(PROBLEM_ARGS, const float *q, const float *k, const float *v,
                     double *o, double *lse, int64_t *pairs, int nthreads)
 {
     PROBLEM_INIT;
+    return hstu_fwd_impl(&p, NULL, q, k, v, o, lse, pairs, nthreads);
+}
+
+/* The same with the relative attention bias (self-attention only): ts [tokens]
+ * or NULL, time_tab [H][11] (with ts), pos_tab [H][P] or NULL. */
+int oracle_hstu_fwd_rab(PROBLEM_ARGS, const int32_t *ts, const double *time_tab, const double *pos_tab,
+                        int P, const float *q, const float *k, const float *v, double *o, double *lse,
+                        int64_t *pairs, int nthreads)
+{
+    PROBLEM_INIT;
+    if (cross || (pos_tab && P < 1) || (ts && !time_tab)) return 1;
+    rab_t r = {ts, time_tab, pos_tab, P};
+    return hstu_fwd_impl(&p, &r, q, k, v, o, lse, pairs, nthreads);
+}
+
+static int hstu_fwd_impl(const problem_t *pp, const rab_t *rab, const float *q, const float *k,
+                         const float *v, double *o, double *lse, int64_t *pairs, int nthreads)
+{
+    const problem_t p = *pp;
+    const int B = p.B, H = p.H, Dqk = p.Dqk, Dv = p.Dv, softmax = p.softmax, cross = p.cross,
+              causal = p.causal;
+    const int32_t *num_targets = p.num_targets;
     if (check(&p)) return 1;
     double al = alpha_of(&p);
     seq_t *seqs = (seq_t *)calloc((size_t)(B > 0 ? B : 1), sizeof(seq_t));
@@ -255,7 +327,7 @@ int oracle_hstu_fwd(PROBLEM_ARGS, const float *q, const float *k, const float *v
             for (int r = 0; r < rows; ++r) {
                 int h = r % H, i = r / H;
                 int64_t tok = s->q0 + i;
-                row_forward(s, h, i, mask + (int64_t)i * s->S_kv, H, Dqk, Dv, softmax, al, q, k, v,
+                row_forward(s, h, i, mask + (int64_t)i * s->S_kv, H, Dqk, Dv, softmax, al, q, k, v, rab,
                             o + (tok * H + h) * Dv, lse ? lse + tok * H + h : NULL, sbuf);
             }
             free(sbuf);
@@ -299,7 +371,7 @@ int oracle_hstu_rows(PROBLEM_ARGS, const float *q, const float *k, const float *
         for (int r = 0; r < n; ++r) {
             const seq_t *s = &seqs[rows_b[r]];
             for (int j = 0; j < s->S_kv; ++j) mrow[j] = (unsigned char)visible(s, rows_i[r], j);
-            row_forward(s, rows_h[r], rows_i[r], mrow, H, Dqk, Dv, softmax, al, q, k, v,
+            row_forward(s, rows_h[r], rows_i[r], mrow, H, Dqk, Dv, softmax, al, q, k, v, NULL,
                         o_rows + (int64_t)r * Dv, lse_rows ? lse_rows + r : NULL, sbuf);
         }
         free(sbuf);

@@ -13,6 +13,7 @@ import pytest
 import oracle
 import test_oracle_mask as TM
 import test_oracle_numerics as TN
+import test_oracle_rab as TR
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "hstu_oracle.c")
 
@@ -25,7 +26,13 @@ MUTATIONS = {
     "targets_ignore_minfull": ("full = (s->L == 0) || (s->M > 0);", "full = (s->L == 0);"),
     "cross_top_left": ("x = u + (s->Ukv - s->Uq);", "x = u;"),
     "silu_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
-    "alpha_dropped": ("sbuf[j] = alpha * dot;", "sbuf[j] = dot;"),
+    "alpha_dropped": ("sbuf[j] = alpha * dot +", "sbuf[j] = dot +"),
+    "rab_bucket_strict": ("if (kRabEdges[e] <= d) b = e + 1;", "if (kRabEdges[e] < d) b = e + 1;"),
+    "rab_time_head_zero": ("r->time_tab[(int64_t)h * RAB_BUCKETS", "r->time_tab[(int64_t)0 * RAB_BUCKETS"),
+    "rab_pos_signed": ("int d = i > j ? i - j : j - i;", "int d = i > j ? i - j : 0;"),
+    "rab_pos_clamp": ("imin(d, r->P - 1)", "imin(d, r->P - 2)"),
+    "rab_time_gap_reversed": ("(int64_t)r->ts[s->q0 + i] - (int64_t)r->ts[s->kv0 + j]",
+                              "(int64_t)r->ts[s->q0 + i] + (int64_t)r->ts[s->kv0 + j]"),
     "default_alpha": ("1.0 / sqrt((double)p->Dqk)", "1.0 / (double)p->Dqk"),
     "wrong_head_of_k": ("const float *kj = k + ((s->kv0 + j) * H + h)",
                         "const float *kj = k + ((s->kv0 + j) * H + 0)"),
@@ -63,6 +70,10 @@ def _pins():
             TN.test_attn_scale_default_is_inverse_max_uih_of_group,
             TM.test_mask_matches_enumerator_self_attention,
             TM.test_mask_matches_enumerator_cross_attention]
+    out.append(TR.test_time_buckets_match_the_table)
+    for causal in (True, False):
+        out.append(lambda c=causal: TR.test_softmax_with_bias_equals_sdpa(c, "both"))
+    out += [TR.test_silu_with_bias_equals_dense_product, TR.test_constant_positional_bias_only_shifts_softmax]
     return out
 
 
