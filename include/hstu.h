@@ -55,9 +55,11 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 1
+#define HSTU_ABI_VERSION 2
 #define HSTU_MAX_GROUPS 64
 #define HSTU_MAX_SPLITS 128
+#define HSTU_RAB_TIME_BUCKETS 11 /* time-gap buckets of the relative attention bias */
+#define HSTU_RAB_MAX_POS 2048    /* longest positional bias table */
 
 typedef enum {
     HSTU_OK = 0,
@@ -111,6 +113,18 @@ typedef struct {
                    natural log; -inf for a row that sees no key */
     int32_t schedule; /* work order: 0 = default (2), 1 = q-tile levels heavy-first,
                          2 = per-XCD sequence groups (each (b,h) kept on one XCD's L2) */
+    /* Relative attention bias (HSTU explainer, "The layer, line by line" (b) and "The
+     * relative attention bias"); self-attention only (HSTU_ERR_UNSUPPORTED with cross).
+     * Added to the score before the mask and the non-linearity:
+     *   s[b,h,i,j] = alpha q_i.k_j + rab_pos[h][min(|i - j|, rab_pos_len - 1)]
+     *                              + rab_time[h][bucket(|ts_i - ts_j|)]
+     * i, j: positions in the sequence; bucket(d): how many of the gap edges
+     * 1, 5, 30, 60, 300, 1800, 3600, 86400, 604800, 2600000 (seconds) are <= d.
+     * All NULL: no bias (the fields of ABI version 1 keep their meaning). */
+    const int32_t *rab_timestamps; /* device [tokens of q] int32 seconds; NULL = no time term */
+    const float *rab_time;         /* device [nhead][HSTU_RAB_TIME_BUCKETS], with rab_timestamps */
+    const float *rab_pos;          /* device [nhead][rab_pos_len]; NULL = no positional term */
+    int32_t rab_pos_len;           /* 1 ..= HSTU_RAB_MAX_POS when rab_pos is set */
 } hstu_fwd_args_t;
 
 /* Host-only argument check (no HIP call); also run by every entry point. */

@@ -72,11 +72,15 @@ def load(path: Optional[str] = None):
     lib.oracle_seq_info.argtypes = _PROBLEM + [_i32p, _f64p]
     lib.oracle_hstu_fwd_rab.argtypes = _PROBLEM + [_i32p, _f64p, _f64p, ctypes.c_int, _f32p, _f32p,
                                                    _f32p, _f64p, _f64p, _i64p, ctypes.c_int]
+    lib.oracle_hstu_rows_rab.argtypes = _PROBLEM + [_i32p, _f64p, _f64p, ctypes.c_int, _f32p, _f32p,
+                                                    _f32p, ctypes.c_int, _i32p, _i32p, _i32p, _f64p,
+                                                    _f64p, ctypes.c_int]
     lib.oracle_rab_bucket.argtypes = [ctypes.c_int64]
     lib.oracle_rab_bucket.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     for f in ("oracle_mask", "oracle_hstu_fwd", "oracle_hstu_fwd_rab", "oracle_hstu_rows",
+              "oracle_hstu_rows_rab",
               "oracle_count_pairs", "oracle_seq_info"):
         getattr(lib, f).restype = ctypes.c_int
     if path is None:
@@ -178,6 +182,30 @@ def forward_rab(p: Problem, q, k, v, timestamps=None, time_table=None, pos_table
     if rc != 0:
         raise ValueError("oracle_hstu_fwd_rab rejected its arguments")
     return o, lse, int(pairs[0])
+
+
+def rows_rab(p: Problem, q, k, v, rows_b, rows_h, rows_i, timestamps=None, time_table=None,
+             pos_table=None, nthreads: int = 0, lib=None):
+    """Selected rows with the relative attention bias (arguments as rows() and forward_rab())."""
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    ts = None if timestamps is None else np.ascontiguousarray(timestamps, np.int32)
+    tt = None if time_table is None else np.ascontiguousarray(time_table, np.float64)
+    pt = None if pos_table is None else np.ascontiguousarray(pos_table, np.float64)
+    P = 0 if pt is None else int(pt.shape[1])
+    rb = np.ascontiguousarray(rows_b, np.int32)
+    rh = np.ascontiguousarray(rows_h, np.int32)
+    ri = np.ascontiguousarray(rows_i, np.int32)
+    n = len(rb)
+    o = np.zeros((n, p.Dv), np.float64)
+    lse = np.zeros(n, np.float64) if p.softmax else None
+    rc = lib.oracle_hstu_rows_rab(*p.args(), _ptr(ts, _i32p), _ptr(tt, _f64p), _ptr(pt, _f64p), P,
+                                  _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), n, _ptr(rb, _i32p),
+                                  _ptr(rh, _i32p), _ptr(ri, _i32p), _ptr(o, _f64p), _ptr(lse, _f64p),
+                                  int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_hstu_rows_rab rejected its arguments")
+    return o, lse
 
 
 def rab_bucket(d: int, lib=None) -> int:

@@ -339,6 +339,10 @@ static int hstu_fwd_impl(const problem_t *pp, const rab_t *rab, const float *q, 
     return 0;
 }
 
+static int hstu_rows_impl(const problem_t *pp, const rab_t *rab, const float *q, const float *k,
+                          const float *v, int n, const int32_t *rows_b, const int32_t *rows_h,
+                          const int32_t *rows_i, double *o_rows, double *lse_rows, int nthreads);
+
 /* Selected rows only: row r is (rows_b[r], rows_h[r], rows_i[r]) with i the row inside
  * its sequence.  o_rows: [n][Dv] double; lse_rows (may be NULL): [n] double. */
 int oracle_hstu_rows(PROBLEM_ARGS, const float *q, const float *k, const float *v, int n,
@@ -346,6 +350,27 @@ int oracle_hstu_rows(PROBLEM_ARGS, const float *q, const float *k, const float *
                      double *o_rows, double *lse_rows, int nthreads)
 {
     PROBLEM_INIT;
+    return hstu_rows_impl(&p, NULL, q, k, v, n, rows_b, rows_h, rows_i, o_rows, lse_rows, nthreads);
+}
+
+/* Selected rows with the relative attention bias (arguments as oracle_hstu_fwd_rab). */
+int oracle_hstu_rows_rab(PROBLEM_ARGS, const int32_t *ts, const double *time_tab, const double *pos_tab,
+                         int P, const float *q, const float *k, const float *v, int n,
+                         const int32_t *rows_b, const int32_t *rows_h, const int32_t *rows_i,
+                         double *o_rows, double *lse_rows, int nthreads)
+{
+    PROBLEM_INIT;
+    if (cross || (pos_tab && P < 1) || (ts && !time_tab)) return 1;
+    rab_t r = {ts, time_tab, pos_tab, P};
+    return hstu_rows_impl(&p, &r, q, k, v, n, rows_b, rows_h, rows_i, o_rows, lse_rows, nthreads);
+}
+
+static int hstu_rows_impl(const problem_t *pp, const rab_t *rab, const float *q, const float *k,
+                          const float *v, int n, const int32_t *rows_b, const int32_t *rows_h,
+                          const int32_t *rows_i, double *o_rows, double *lse_rows, int nthreads)
+{
+    const problem_t p = *pp;
+    const int B = p.B, H = p.H, Dqk = p.Dqk, Dv = p.Dv, softmax = p.softmax;
     if (check(&p)) return 1;
     double al = alpha_of(&p);
     seq_t *seqs = (seq_t *)calloc((size_t)(B > 0 ? B : 1), sizeof(seq_t));
@@ -371,7 +396,7 @@ int oracle_hstu_rows(PROBLEM_ARGS, const float *q, const float *k, const float *
         for (int r = 0; r < n; ++r) {
             const seq_t *s = &seqs[rows_b[r]];
             for (int j = 0; j < s->S_kv; ++j) mrow[j] = (unsigned char)visible(s, rows_i[r], j);
-            row_forward(s, rows_h[r], rows_i[r], mrow, H, Dqk, Dv, softmax, al, q, k, v, NULL,
+            row_forward(s, rows_h[r], rows_i[r], mrow, H, Dqk, Dv, softmax, al, q, k, v, rab,
                         o_rows + (int64_t)r * Dv, lse_rows ? lse_rows + r : NULL, sbuf);
         }
         free(sbuf);

@@ -90,7 +90,8 @@ class _Call:
     """The hstu_fwd_args_t of one call plus the objects it points into."""
 
     def __init__(self, q, k, v, *, seq_offsets, seq_offsets_kv, num_targets, max_seqlen_q,
-                 max_seqlen_kv, cross, causal, softmax, alpha, groups, return_lse, out, schedule):
+                 max_seqlen_kv, cross, causal, softmax, alpha, groups, return_lse, out, schedule,
+                 rab_timestamps=None, rab_time=None, rab_pos=None):
         for t, n in ((q, "q"), (k, "k"), (v, "v")):
             if not t.is_cuda:
                 raise ValueError(f"{n} must be a device tensor")
@@ -139,7 +140,8 @@ class _Call:
             self.lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
         self.out = out
         self.groups = _groups_c(groups)
-        self.keep = (q, k, v, seq_offsets, seq_offsets_kv, num_targets)
+        _check_rab(rab_timestamps, rab_time, rab_pos, H, total_q)
+        self.keep = (q, k, v, seq_offsets, seq_offsets_kv, num_targets, rab_timestamps, rab_time, rab_pos)
         a = _abi.FwdArgsC()
         a.dtype, a.batch, a.nhead, a.hdim_qk, a.hdim_v = dt, B, H, Dqk, Dv
         a.jagged, a.cross = int(jagged), int(bool(cross))
@@ -157,6 +159,10 @@ class _Call:
         a.groups = ctypes.cast(self.groups, ctypes.POINTER(_abi.MaskGroupC))
         a.lse = _ptr(self.lse)
         a.schedule = int(schedule)
+        a.rab_timestamps = _ptr(rab_timestamps)
+        a.rab_time = _ptr(rab_time)
+        a.rab_pos = _ptr(rab_pos)
+        a.rab_pos_len = 0 if rab_pos is None else int(rab_pos.shape[-1])
         self.args = a
         self.device = q.device
 
@@ -166,6 +172,22 @@ class _Call:
         return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _check_rab(ts, tt, pt, H, total_q):
+    """Shapes and types of the relative attention bias inputs (the library checks the rest)."""
+    if ts is not None:
+        if ts.dtype != torch.int32 or not ts.is_cuda or not ts.is_contiguous() or ts.numel() != total_q:
+            raise ValueError("rab_timestamps must be a contiguous int32 device tensor, one per q token")
+        if tt is None:
+            raise ValueError("rab_timestamps needs rab_time")
+    if tt is not None and (tt.dtype != torch.float32 or not tt.is_cuda or not tt.is_contiguous()
+                           or tuple(tt.shape) != (H, _abi.HSTU_RAB_TIME_BUCKETS)):
+        raise ValueError(f"rab_time must be a contiguous float32 device tensor [{H}, "
+                         f"{_abi.HSTU_RAB_TIME_BUCKETS}]")
+    if pt is not None and (pt.dtype != torch.float32 or not pt.is_cuda or not pt.is_contiguous()
+                           or pt.dim() != 2 or pt.shape[0] != H):
+        raise ValueError(f"rab_pos must be a contiguous float32 device tensor [{H}, P]")
+
+
 def _result(call, return_lse):
     return (call.out, call.lse) if return_lse else call.out
 
@@ -173,15 +195,19 @@ def _result(call, return_lse):
 def hstu_fwd(q, k, v, *, seq_offsets=None, seq_offsets_kv=None, num_targets=None,
              max_seqlen_q=None, max_seqlen_kv=None, cross=False, causal=True, softmax=False,
              alpha=0.0, groups=(HstuGroup(),), return_lse=False, out=None, schedule=0,
-             stream=None):
+             rab_timestamps=None, rab_time=None, rab_pos=None, stream=None):
     """HSTU attention forward.  Batched: q [B, S_q, H, Dqk], k [B, S_kv, H, Dqk],
     v [B, S_kv, H, Dv].  Jagged: q/k/v [total, H, D] with int32 seq_offsets [B+1]
-    (device) and max_seqlen_q.  Returns o (and the LSE when return_lse)."""
+    (device) and max_seqlen_q.  Returns o (and the LSE when return_lse).
+    Relative attention bias (self-attention): rab_timestamps int32 [tokens of q]
+    with rab_time float32 [H, 11] (time-gap buckets), rab_pos float32 [H, P]
+    (positional, indexed by min(|i - j|, P - 1))."""
     lib = _abi.load()
     c = _Call(q, k, v, seq_offsets=seq_offsets, seq_offsets_kv=seq_offsets_kv,
               num_targets=num_targets, max_seqlen_q=max_seqlen_q, max_seqlen_kv=max_seqlen_kv,
               cross=cross, causal=causal, softmax=softmax, alpha=alpha, groups=groups,
-              return_lse=return_lse, out=out, schedule=schedule)
+              return_lse=return_lse, out=out, schedule=schedule, rab_timestamps=rab_timestamps,
+              rab_time=rab_time, rab_pos=rab_pos)
     _abi.check(lib.hstu_fwd(ctypes.byref(c.args), None, 0, c.stream(stream)))
     return _result(c, return_lse)
 
@@ -195,7 +221,8 @@ def workspace_size(q, k, v, num_splits, **kw) -> int:
 def _call_kw(kw):
     d = dict(seq_offsets=None, seq_offsets_kv=None, num_targets=None, max_seqlen_q=None,
              max_seqlen_kv=None, cross=False, causal=True, softmax=False, alpha=0.0,
-             groups=(HstuGroup(),), return_lse=False, out=None, schedule=0)
+             groups=(HstuGroup(),), return_lse=False, out=None, schedule=0, rab_timestamps=None,
+             rab_time=None, rab_pos=None)
     d.update(kw)
     return d
 

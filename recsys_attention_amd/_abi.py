@@ -20,7 +20,9 @@ HSTU_FP16 = 0
 HSTU_BF16 = 1
 HSTU_MAX_GROUPS = 64
 HSTU_MAX_SPLITS = 128
-HSTU_ABI_VERSION = 1
+HSTU_ABI_VERSION = 2
+HSTU_RAB_TIME_BUCKETS = 11
+HSTU_RAB_MAX_POS = 2048
 
 # every symbol include/hstu.h declares
 EXPORTED = ("hstu_validate_args", "hstu_fwd_workspace_size", "hstu_fwd", "hstu_fwd_splitkv",
@@ -49,7 +51,9 @@ class FwdArgsC(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("softmax", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("num_groups", ctypes.c_int32),
                 ("groups", ctypes.POINTER(MaskGroupC)), ("lse", ctypes.c_void_p),
-                ("schedule", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32),
+                ("rab_timestamps", ctypes.c_void_p), ("rab_time", ctypes.c_void_p),
+                ("rab_pos", ctypes.c_void_p), ("rab_pos_len", ctypes.c_int32)]
 
 
 _lib = None

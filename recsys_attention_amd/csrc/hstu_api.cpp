@@ -107,6 +107,15 @@ hstu_status_t validate(const hstu_fwd_args_t *a) {
             return fail(HSTU_ERR_INVALID_ARG, "group %d: attn_scale 0 needs max_uih_q >= 0", g);
     }
     if (!isfinite(a->alpha)) return fail(HSTU_ERR_INVALID_ARG, "alpha not finite");
+    if (a->rab_timestamps || a->rab_pos) {
+        if (a->cross) return fail(HSTU_ERR_UNSUPPORTED, "the relative attention bias is for self-attention");
+        if (a->rab_timestamps && (!a->rab_time || ((uintptr_t)a->rab_time & 3u) ||
+                                  ((uintptr_t)a->rab_timestamps & 3u)))
+            return fail(HSTU_ERR_INVALID_ARG, "rab_timestamps needs a 4-byte aligned rab_time table");
+        if (a->rab_pos && (a->rab_pos_len < 1 || a->rab_pos_len > HSTU_RAB_MAX_POS || ((uintptr_t)a->rab_pos & 3u)))
+            return fail(HSTU_ERR_INVALID_ARG, "rab_pos_len %d not in 1..%d (or rab_pos misaligned)", a->rab_pos_len,
+                        HSTU_RAB_MAX_POS);
+    }
     if (a->lse && !a->softmax) return fail(HSTU_ERR_INVALID_ARG, "lse output is for the softmax variant");
     if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(HSTU_ERR_INVALID_ARG, "lse must be 4-byte aligned");
     return HSTU_OK;
@@ -141,6 +150,10 @@ void fill_params(const hstu_fwd_args_t *a, int32_t num_splits, hstu::KernelParam
     p.num_splits = num_splits;
     p.schedule = a->schedule == 0 ? 2 : a->schedule;
     p.alpha = a->alpha != 0.0f ? a->alpha : (float)(1.0 / sqrt((double)a->hdim_qk));
+    p.rab_ts = a->rab_timestamps;
+    p.rab_time = a->rab_timestamps ? a->rab_time : nullptr;
+    p.rab_pos = a->rab_pos;
+    p.rab_pos_len = a->rab_pos ? a->rab_pos_len : 0;
     p.G = a->num_groups;
     p.per_group = a->batch > 0 ? a->batch / a->num_groups : 1;
     for (int g = 0; g < a->num_groups; ++g) {

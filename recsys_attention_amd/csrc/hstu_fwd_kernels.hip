@@ -221,6 +221,16 @@ __device__ __forceinline__ void load_to_lds(const i32x4_t &rsrc, uint32_t lds_wa
         : "s"(lds_wave), "v"(off), "s"(rsrc)
         : "m0");
 }
+// 4 bytes per lane, landing at lds_wave + 4 i (same rules as load_to_lds).
+__device__ __forceinline__ void load_to_lds4(const i32x4_t &rsrc, uint32_t lds_wave, uint32_t off) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds"
+        :
+        : "s"(lds_wave), "v"(off), "s"(rsrc)
+        : "m0");
+}
 #pragma clang diagnostic pop
 
 // Transposed LDS read of 4 16-bit elements (gfx950): within each group of 16
@@ -251,6 +261,45 @@ __device__ __forceinline__ void wait_all_loads_here() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 #pragma clang diagnostic pop
+
+// Relative attention bias (HSTU explainer, "The relative attention bias").
+
+// One 32-key block of raw scores x = q.k of this lane's row -> the biased score
+// in the non-linearity's domain: x <- ac x + pos[min(|row - j|, pmax)] + time[bucket(|t_row - t_j|)].
+// Element i is key key0 + 8(i/4) + i%4; ts4 points at that key0's timestamp in
+// the LDS copy of the tile's key timestamps (16-byte aligned).  The tables are
+// already multiplied by the domain factor (1 for SiLU, log2 e for softmax).
+__device__ __forceinline__ void rab_block(f32x16_t &x, float ac, int row, int key0, const float *pos,
+                                          int pmax, const int32_t *ts4, int32_t t_row, const float *tt,
+                                          bool has_pos, bool has_time) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        i32x4_t tk = {};
+        if (has_time) tk = *(const i32x4_t *)(ts4 + 8 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            float b = 0.0f;
+            if (has_pos) {
+                const int j = key0 + 8 * q4 + e;
+                b = pos[imin(row > j ? row - j : j - row, pmax)];
+            }
+            if (has_time) {
+                // |t_row - t_j| is exact in 32-bit unsigned arithmetic for any two int32 values
+                const uint32_t a = (uint32_t)t_row, c = (uint32_t)tk[e];
+                const uint32_t d = t_row >= tk[e] ? a - c : c - a;
+                // time-gap bucket edges in seconds: a gap's bucket is how many edges are <= it
+                constexpr uint32_t kEdges[HSTU_RAB_TIME_BUCKETS - 1] = {1u,    5u,    30u,    60u,     300u,
+                                                                        1800u, 3600u, 86400u, 604800u, 2600000u};
+                float tb = tt[0];
+#pragma unroll
+                for (int k = 0; k < HSTU_RAB_TIME_BUCKETS - 1; ++k) tb = d >= kEdges[k] ? tt[k + 1] : tb;
+                b += tb;
+            }
+            x[i] = fmaf(x[i], ac, b);
+        }
+    }
+}
 
 // SiLU of one score without the factor alpha (see silu_block), unmasked.
 __device__ __forceinline__ float silu_raw(float v, float neg_alpha_log2e) {
@@ -335,7 +384,11 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     for (int i = 0; i < 8; ++i) oacc[i & 3] = E::mfma(op1[i], p1[i >> 2], oacc[i & 3]);
 }
 
-template <int DT, int D, bool SOFTMAX, bool SPLIT, int DV = D>
+// RAB: relative attention bias.  The bias is added to alpha q.k before the mask
+// and the non-linearity, so in that variant the scores carry alpha themselves
+// (SiLU of the biased score, epilogue without alpha) instead of folding it into
+// the exponent and the epilogue.
+template <int DT, int D, bool SOFTMAX, bool SPLIT, int DV = D, bool RAB = false>
 __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
     constexpr int NW = waves_for(D);
@@ -349,6 +402,11 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     // two stages of [K tile | V tile]
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][C::STAGE];
     __shared__ int32_t red[2 * NW];
+    // bias only: the head's positional table and each stage's key timestamps
+    // (at least 64 entries: one wave-load)
+    constexpr int TSN = RAB ? (BN < 64 ? 64 : BN) : 1;
+    __shared__ float pos_lds[RAB ? HSTU_RAB_MAX_POS : 1];
+    __shared__ __attribute__((aligned(16))) int32_t ts_lds[2][TSN];
 
     BlockPlan bp;
     if (!plan_block<BN, NW>(p, SPLIT, bp, red)) return;
@@ -400,8 +458,42 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         v_lane[c] = (uint32_t)row * vs2 + (uint32_t)(pc ^ (kVSwz * (row & 3))) * 16;
     }
     // LDS byte address of this wave's first landing slot (wave-uniform)
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] +
-                              (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] + (uint32_t)wave_u * 1024;
+
+    // ---- relative attention bias set-up
+    const bool has_pos = RAB && p.rab_pos != nullptr, has_time = RAB && p.rab_ts != nullptr;
+    constexpr float kDom = SOFTMAX ? kLog2e : 1.0f;  // the non-linearity's domain factor
+    float tt[HSTU_RAB_TIME_BUCKETS];
+    int32_t t_row = 0;
+    i32x4_t tsr = {};
+    const int pmax = has_pos ? p.rab_pos_len - 1 : 0;
+    if constexpr (RAB) {
+        if (has_pos) {
+            const float *ph = p.rab_pos + (int64_t)h * p.rab_pos_len;
+            for (int i = tid; i < p.rab_pos_len; i += C::NT) pos_lds[i] = ph[i] * kDom;
+        }
+#pragma unroll
+        for (int k = 0; k < HSTU_RAB_TIME_BUCKETS; ++k) tt[k] = 0.0f;
+        if (has_time) {
+#pragma unroll
+            for (int k = 0; k < HSTU_RAB_TIME_BUCKETS; ++k)
+                tt[k] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                                                      int32_t, p.rab_time[h * HSTU_RAB_TIME_BUCKETS + k]))) *
+                        kDom;
+            t_row = bp.row < s.S_q ? p.rab_ts[s.q0 + bp.row] : 0;
+            tsr = make_rsrc_words(p.rab_ts + s.kv0, (uint32_t)s.S_kv * 4u);
+        }
+    }
+    const uint32_t ts_base = (uint32_t)(uintptr_t)(lds_void_t *)&ts_lds[0][0];
+    // the key timestamps of tile t into stage b: wave w < TSN / 64 loads 64 of them
+    auto issue_ts = [&](int t, int b) {
+        if constexpr (RAB) {
+            if (has_time && wave_u < TSN / 64)
+                load_to_lds4(tsr, ts_base + (uint32_t)(b * TSN + wave_u * 64) * 4u,
+                             (uint32_t)(t * BN + wave_u * 64 + lane) * 4u);
+        }
+    };
     // load idx of key tile t into stage b: idx < LOADS are K chunks, the rest V
     constexpr int LPT = C::LOADS + C::LOADS_V;  // loads per tile and wave
     auto issue_one = [&](int t, int b, int idx) {
@@ -418,6 +510,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     auto issue_loads = [&](int t, int b) {
 #pragma unroll
         for (int idx = 0; idx < LPT; ++idx) issue_one(t, b, idx);
+        issue_ts(t, b);
     };
 
     // ---- per-lane LDS read addresses (stage 0; stage 1 adds 2 * TILE_BYTES)
@@ -442,8 +535,9 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;
-    const float neg_alpha_log2e = -p.alpha * kLog2e;
-    const float sc_soft = p.alpha * kLog2e;
+    // with the bias the scores already carry alpha (rab_block)
+    const float neg_alpha_log2e = RAB ? -kLog2e : -p.alpha * kLog2e;
+    const float sc_soft = RAB ? 1.0f : p.alpha * kLog2e;
     const uint8_t *lds0 = &lds[0][0];
 
     if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
@@ -462,7 +556,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
         const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
 
-        if constexpr (!SOFTMAX && D == 128 && DV == 128) {
+        if constexpr (!SOFTMAX && !RAB && D == 128 && DV == 128) {
             if (wave_any && !wave_mask) {
                 silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc,
                                           neg_alpha_log2e, [&](int idx) {
@@ -494,6 +588,12 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
             // ---- mask + non-linearity; element i of block kb is key
             //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
+            if constexpr (RAB) {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+                    rab_block(sacc[kb], p.alpha * kDom, bp.row, j0 + kb * 32 + 4 * g, pos_lds, pmax,
+                              &ts_lds[buf][kb * 32 + 4 * g], t_row, tt, has_pos, has_time);
+            }
             if constexpr (!SOFTMAX) {
                 // p = x sigmoid(alpha x); the factor alpha of SiLU(alpha x) goes into the epilogue
                 if (wave_mask) {
@@ -568,7 +668,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     }
 
     // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
-    float scale = s.attn_scale * p.alpha;
+    float scale = RAB ? s.attn_scale : s.attn_scale * p.alpha;
     float lse_val = 0.f;
     if constexpr (SOFTMAX) {
         const float l = l_run + __shfl_xor(l_run, 32);
@@ -738,8 +838,12 @@ template <int DT, int D, int DV, bool SOFTMAX, bool SPLIT>
 static hipError_t launch_one(const KernelParams &p, hipStream_t stream) {
     const int64_t grid = grid_size(p);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV>), dim3((unsigned)grid), dim3(64 * waves_for(D)),
-                       0, stream, p);
+    if (p.rab_pos != nullptr || p.rab_ts != nullptr)
+        hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, true>), dim3((unsigned)grid),
+                           dim3(64 * waves_for(D)), 0, stream, p);
+    else
+        hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, false>), dim3((unsigned)grid),
+                           dim3(64 * waves_for(D)), 0, stream, p);
     return hipGetLastError();
 }
 

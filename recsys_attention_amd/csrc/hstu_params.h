@@ -33,6 +33,11 @@ struct KernelParams {
     float alpha;                  // resolved QK scale
     int32_t G, per_group;
     GroupDev groups[HSTU_MAX_GROUPS];
+    // relative attention bias (nullptr: term absent)
+    const int32_t *rab_ts;   // [tokens] timestamps
+    const float *rab_time;   // [H][HSTU_RAB_TIME_BUCKETS]
+    const float *rab_pos;    // [H][rab_pos_len]
+    int32_t rab_pos_len;
 };
 
 }  // namespace hstu

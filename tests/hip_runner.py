@@ -51,16 +51,28 @@ class DeviceInputs:
                        cross=w.cross, causal=w.causal, softmax=w.softmax, alpha=w.alpha,
                        groups=hip_groups(w))
 
-    def forward(self, num_splits=1, schedule=0, return_lse=None, out=None, workspace=None):
+    def forward(self, num_splits=1, schedule=0, return_lse=None, out=None, workspace=None,
+                rab=None):
         rl = self.w.softmax if return_lse is None else return_lse
+        kw = dict(self.kw)
+        if rab is not None:
+            kw.update(rab_kwargs(rab, self.q.device))
         if num_splits == 1:
             return hip.hstu_fwd(self.q, self.k, self.v, return_lse=rl, schedule=schedule, out=out,
-                                **self.kw)
+                                **kw)
         return hip.hstu_fwd_splitkv(self.q, self.k, self.v, num_splits, return_lse=rl,
-                                    schedule=schedule, out=out, workspace=workspace, **self.kw)
+                                    schedule=schedule, out=out, workspace=workspace, **kw)
 
     def count_pairs(self, schedule=0):
         return hip.hstu_count_visible_pairs(self.q, self.k, self.v, schedule=schedule, **self.kw)
+
+
+def rab_kwargs(rab, device="cuda"):
+    """workloads.RabInputs -> the binding's rab_* arguments (device tensors)."""
+    def dev(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    return dict(rab_timestamps=dev(rab.timestamps), rab_time=dev(rab.time_table),
+                rab_pos=dev(rab.pos_table))
 
 
 def o_tokens(w, o: torch.Tensor) -> np.ndarray:

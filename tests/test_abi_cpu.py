@@ -57,6 +57,10 @@ def _args(**over):
 
 def test_valid_args_pass(lib):
     assert lib.hstu_validate_args(ctypes.byref(_args())) == _abi.HSTU_OK
+    rab = dict(rab_timestamps=0xb0000, rab_time=0xc0000, rab_pos=0xa0000,
+               rab_pos_len=_abi.HSTU_RAB_MAX_POS)
+    assert lib.hstu_validate_args(ctypes.byref(_args(**rab))) == _abi.HSTU_OK
+    assert lib.hstu_validate_args(ctypes.byref(_args(rab_pos=0xa0000, rab_pos_len=1))) == _abi.HSTU_OK
 
 
 @pytest.mark.parametrize("over,status", [
@@ -82,6 +86,12 @@ def test_valid_args_pass(lib):
     (dict(causal=2), _abi.HSTU_ERR_INVALID_ARG),
     (dict(schedule=3), _abi.HSTU_ERR_INVALID_ARG),
     (dict(jagged=0, seqlen_kv=5), _abi.HSTU_ERR_INVALID_ARG),  # batched self needs equal lengths
+    # relative attention bias
+    (dict(cross=1, seq_offsets_kv=0x58000, rab_pos=0xa0000, rab_pos_len=8), _abi.HSTU_ERR_UNSUPPORTED),
+    (dict(rab_timestamps=0xb0000), _abi.HSTU_ERR_INVALID_ARG),              # no time table
+    (dict(rab_timestamps=0xb0002, rab_time=0xc0000), _abi.HSTU_ERR_INVALID_ARG),  # misaligned
+    (dict(rab_pos=0xa0000, rab_pos_len=0), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(rab_pos=0xa0000, rab_pos_len=_abi.HSTU_RAB_MAX_POS + 1), _abi.HSTU_ERR_INVALID_ARG),
 ])
 def test_invalid_args_rejected(lib, over, status):
     a = _args(**over)

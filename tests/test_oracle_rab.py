@@ -122,3 +122,21 @@ def test_cross_attention_is_rejected():
     q, k, v = _rand((4, 1, 32), 1), _rand((9, 1, 32), 2), _rand((9, 1, 32), 3)
     with pytest.raises(ValueError):
         oracle.forward_rab(p, q, k, v, pos_table=np.zeros((1, 3)))
+
+
+def test_selected_rows_with_bias_equal_whole_forward():
+    """The oracle's row-at-a-time entry (used for sampled parity at full size) gives
+    the whole forward's rows, bias included."""
+    B, H, D, S = 2, 3, 32, 41
+    q, k, v, ts, time_tab, pos_tab = _inputs(B, H, D, S, 71)
+    for softmax in (False, True):
+        p = _problem(B, H, D, S, causal=True, softmax=softmax, alpha=0.3, a=0.5)
+        o, lse, _ = oracle.forward_rab(p, q, k, v, timestamps=ts, time_table=time_tab,
+                                       pos_table=pos_tab)
+        rb, rh, ri = [0, 1, 1, 0], [2, 0, 1, 1], [40, 0, 17, 5]
+        orow, lrow = oracle.rows_rab(p, q, k, v, rb, rh, ri, timestamps=ts, time_table=time_tab,
+                                     pos_table=pos_tab)
+        for n, (b, h, i) in enumerate(zip(rb, rh, ri)):
+            assert np.array_equal(orow[n], o[b * S + i, h])
+            if softmax:
+                assert lrow[n] == lse[b * S + i, h]

@@ -256,3 +256,56 @@ def random_workload(seed: int, *, dtype="bf16", hdim_qk=128, hdim_v=None, batch=
                  hdim_v=hdim_v, jagged=jagged, cross=cross, causal=causal, softmax=softmax,
                  alpha=0.0, groups=groups, uih_q=U, targets=T, uih_kv=Ukv, dist=dist, rng=rng,
                  num_splits=num_splits)
+
+
+# ----------------------------------------------------------------------------
+# relative attention bias inputs
+# ----------------------------------------------------------------------------
+
+# Gaps between consecutive events, in seconds: from same-second bursts to months,
+# so that every time-gap bucket of the bias occurs within a sequence.
+RAB_GAPS = (0, 1, 2, 4, 7, 20, 45, 100, 600, 2000, 5000, 40000, 200000, 900000, 3000000)
+# relative frequencies (long gaps rarer; mean gap about 58000 s, so 8000 events
+# stay well inside int32 epoch seconds)
+RAB_GAP_WEIGHTS = (4, 4, 4, 4, 4, 4, 4, 4, 4, 4, 4, 3, 2, 1, 0.5)
+
+
+@dataclasses.dataclass
+class RabInputs:
+    timestamps: Optional[np.ndarray]  # int32 [tokens of q], or None
+    time_table: Optional[np.ndarray]  # float32 [H, 11], or None
+    pos_table: Optional[np.ndarray]   # float32 [H, P], or None
+
+
+def rab_inputs(w: Workload, seed: int, *, time=True, pos_len: Optional[int] = 64,
+               shuffle=False, extremes=False) -> RabInputs:
+    """Seeded bias inputs for a self-attention workload.
+
+    Draw order: timestamps -> time table -> positional table, from
+    ``numpy.random.default_rng(seed)``.  Timestamps of a sequence start at a
+    random epoch second in [1.4e9, 1.6e9] and grow by gaps drawn from RAB_GAPS
+    (shuffle: the sequence's timestamps are permuted, so gaps occur in both
+    directions; extremes: the sequence's first two tokens are set to -2^31 and
+    2^31 - 1).  Gaps are drawn with the relative frequencies RAB_GAP_WEIGHTS.  Tables are N(0, 1) float32 (the kernel's table dtype)."""
+    rng = np.random.default_rng(seed)
+    ts = None
+    if time:
+        ts = np.zeros(w.total_q, np.int64)
+        for b in range(w.batch):
+            a, e = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+            n = e - a
+            if n == 0:
+                continue
+            gp = np.asarray(RAB_GAP_WEIGHTS, np.float64)
+            t = int(rng.integers(1_400_000_000, 1_600_000_000)) + np.concatenate(
+                [[0], np.cumsum(rng.choice(RAB_GAPS, size=n - 1, p=gp / gp.sum()))])
+            if shuffle:
+                t = rng.permutation(t)
+            if extremes and n >= 2:
+                t[0], t[1] = -2 ** 31, 2 ** 31 - 1
+            ts[a:e] = t
+        assert ts.min() >= -2 ** 31 and ts.max() < 2 ** 31
+        ts = ts.astype(np.int32)
+    tt = rng.standard_normal((w.nhead, 11)).astype(np.float32) if time else None
+    pt = rng.standard_normal((w.nhead, pos_len)).astype(np.float32) if pos_len else None
+    return RabInputs(ts, tt, pt)
