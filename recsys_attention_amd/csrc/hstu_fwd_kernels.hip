@@ -263,14 +263,70 @@ __device__ __forceinline__ void wait_all_loads_here() {
 #pragma clang diagnostic pop
 
 // Relative attention bias (HSTU explainer, "The relative attention bias").
+// |a - b| of two int32 values: exact in 32-bit unsigned arithmetic.
+__device__ __forceinline__ uint32_t abs_gap(int32_t a, int32_t b) {
+    return a >= b ? (uint32_t)a - (uint32_t)b : (uint32_t)b - (uint32_t)a;
+}
+// Time-gap buckets: the bucket of a gap d (seconds) is how many of the edges
+// 1, 5, 30, 60, 300, 1800, 3600, 86400, 604800, 2600000 are <= d.  No two edges
+// share a binade [2^L, 2^(L+1)), so per binade the bucket is lo or lo + 1
+// (lo: edges <= 2^L) with one threshold between them.  The per-head lookup
+// table has one 16-byte entry per binade: entry 0 is d = 0, entry L + 1 covers
+// [2^L, 2^(L+1)); fields {threshold, value below it, value from it on,
+// bucket below | bucket from it on << 8}.
+constexpr int kRabBinades = 33;
+__device__ __forceinline__ int rab_binade(uint32_t d) { return 32 - __clz(d); }
+__device__ __forceinline__ void rab_binade_entry(int idx, const float *tab, u32x4_t *out) {
+    constexpr uint32_t kEdges[HSTU_RAB_TIME_BUCKETS - 1] = {1u,    5u,    30u,    60u,     300u,
+                                                            1800u, 3600u, 86400u, 604800u, 2600000u};
+    const uint32_t dmin = idx == 0 ? 0u : (1u << (idx - 1));
+    int lo = 0;
+#pragma unroll
+    for (int k = 0; k < HSTU_RAB_TIME_BUCKETS - 1; ++k) lo += dmin >= kEdges[k] ? 1 : 0;
+    uint32_t thr = 0xffffffffu;
+#pragma unroll
+    for (int k = 0; k < HSTU_RAB_TIME_BUCKETS - 1; ++k) thr = k == lo ? kEdges[k] : thr;
+    const int hi = imin(lo + 1, HSTU_RAB_TIME_BUCKETS - 1);
+    *out = u32x4_t{thr, __float_as_uint(tab[lo]), __float_as_uint(tab[hi]),
+                   (uint32_t)lo | ((uint32_t)hi << 8)};
+}
+// bucket of d and its table value from the binade table (LDS)
+__device__ __forceinline__ float rab_time_value(uint32_t d, const u32x4_t *oct) {
+    const u32x4_t e = oct[rab_binade(d)];
+    return __uint_as_float(d >= e.x ? e.z : e.y);
+}
+__device__ __forceinline__ int rab_bucket_of(uint32_t d, const u32x4_t *oct) {
+    const u32x4_t e = oct[rab_binade(d)];
+    return (int)(d >= e.x ? e.w >> 8 : e.w & 0xffu);
+}
 
-// One 32-key block of raw scores x = q.k of this lane's row -> the biased score
-// in the non-linearity's domain: x <- ac x + pos[min(|row - j|, pmax)] + time[bucket(|t_row - t_j|)].
+// Wave-wide minimum / maximum through DPP (quad permutes and row rotations give
+// every lane its 16-lane row's result; four lane reads combine the rows).
+__device__ __forceinline__ int32_t wave_min_dpp(int32_t x) {
+    x = imin(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    x = imin(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    x = imin(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));  // row_ror 4
+    x = imin(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));  // row_ror 8
+    return imin(imin(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+                imin(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+__device__ __forceinline__ int32_t wave_max_dpp(int32_t x) {
+    x = imax(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+    x = imax(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+    x = imax(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));
+    x = imax(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+    return imax(imax(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+                imax(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Element-wise bias of one 32-key block of raw scores x = q.k of this lane's row
+// -> the biased score in the non-linearity's domain:
+//   x <- ac x + pos[min(|row - j|, pmax)] + time[bucket(|t_row - t_j|)].
 // Element i is key key0 + 8(i/4) + i%4; ts4 points at that key0's timestamp in
-// the LDS copy of the tile's key timestamps (16-byte aligned).  The tables are
-// already multiplied by the domain factor (1 for SiLU, log2 e for softmax).
+// the LDS copy of the tile's key timestamps (16-byte aligned).  The tables hold
+// the bias as given (softmax takes the biased score to the log2 domain after).
 __device__ __forceinline__ void rab_block(f32x16_t &x, float ac, int row, int key0, const float *pos,
-                                          int pmax, const int32_t *ts4, int32_t t_row, const float *tt,
+                                          int pmax, const int32_t *ts4, int32_t t_row, const u32x4_t *oct,
                                           bool has_pos, bool has_time) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -284,20 +340,99 @@ __device__ __forceinline__ void rab_block(f32x16_t &x, float ac, int row, int ke
                 const int j = key0 + 8 * q4 + e;
                 b = pos[imin(row > j ? row - j : j - row, pmax)];
             }
-            if (has_time) {
-                // |t_row - t_j| is exact in 32-bit unsigned arithmetic for any two int32 values
-                const uint32_t a = (uint32_t)t_row, c = (uint32_t)tk[e];
-                const uint32_t d = t_row >= tk[e] ? a - c : c - a;
-                // time-gap bucket edges in seconds: a gap's bucket is how many edges are <= it
-                constexpr uint32_t kEdges[HSTU_RAB_TIME_BUCKETS - 1] = {1u,    5u,    30u,    60u,     300u,
-                                                                        1800u, 3600u, 86400u, 604800u, 2600000u};
-                float tb = tt[0];
-#pragma unroll
-                for (int k = 0; k < HSTU_RAB_TIME_BUCKETS - 1; ++k) tb = d >= kEdges[k] ? tt[k + 1] : tb;
-                b += tb;
-            }
+            if (has_time) b += rab_time_value(abs_gap(t_row, tk[e]), oct);
             x[i] = fmaf(x[i], ac, b);
         }
+    }
+}
+
+// The bias of one key tile (keys j0 .. j0 + BN - 1) for this lane's row, with the
+// two terms taken per tile where the tile allows it:
+//  * time: the tile's smallest and largest key timestamps bound every gap of the
+//    row; when both bounds fall into one bucket (for every row of the wave), the
+//    time term is one value per row for the whole tile;
+//  * position: in a tile wholly below the wave's rows (every key <= every row)
+//    or wholly above them, |row - j| runs linearly over the tile's keys, so the
+//    table is read at one per-lane base plus compile-time offsets.  The table in
+//    LDS is padded with copies of its last entry up to P + BN - 1 entries, which
+//    takes the clamp to P - 1 off those reads.
+// Other tiles (the diagonal, gaps across a bucket edge) go element by element.
+// Element (kb, i) is key j0 + 32 kb + 4 g + c with c = 8(i/4) + i%4.
+template <int NKB, int BN>
+__device__ __forceinline__ void rab_tile(f32x16_t *x, float ac, int row, int j0, int g, int wrow0,
+                                         const float *pos, int P, const int32_t *ts, int32_t t_row,
+                                         bool row_valid, int32_t S_kv, const u32x4_t *oct, bool has_pos,
+                                         bool has_time, int lane) {
+    float tv = 0.0f;
+    bool time_tile = true;
+    if (has_time) {
+        int32_t lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+        for (int c = 0; c < (BN + 63) / 64; ++c) {
+            const int k = c * 64 + lane;
+            if (k < BN && j0 + k < S_kv) {
+                const int32_t t = ts[k];
+                lo = imin(lo, t);
+                hi = imax(hi, t);
+            }
+        }
+        lo = wave_min_dpp(lo);
+        hi = wave_max_dpp(hi);
+        uint32_t dlo, dhi;
+        if (t_row >= hi) {
+            dlo = abs_gap(t_row, hi);
+            dhi = abs_gap(t_row, lo);
+        } else if (t_row <= lo) {
+            dlo = abs_gap(lo, t_row);
+            dhi = abs_gap(hi, t_row);
+        } else {
+            dlo = 0u;
+            dhi = max(abs_gap(t_row, lo), abs_gap(hi, t_row));
+        }
+        const bool one = !row_valid || rab_bucket_of(dlo, oct) == rab_bucket_of(dhi, oct);
+        time_tile = __ballot(!one) == 0;
+        tv = rab_time_value(dlo, oct);
+    }
+    if (!time_tile) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            rab_block(x[kb], ac, row, j0 + kb * 32 + 4 * g, pos, P - 1, ts + kb * 32 + 4 * g, t_row, oct,
+                      has_pos, has_time);
+        return;
+    }
+    if (has_pos && wrow0 - j0 >= BN - 1) {
+        // below: index row - j = (row - j0) - 4g - c, read at base + (BN - 5 - c) >= 0
+        const int base = imin(row - j0, P + BN - 2) - 4 * g - (BN - 5);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c = 32 * kb + 8 * (i >> 2) + (i & 3);
+                x[kb][i] = fmaf(x[kb][i], ac, pos[base + (BN - 5 - c)] + tv);
+            }
+    } else if (has_pos && wrow0 + 31 < j0) {
+        // above: index j - row = (j0 - row) + 4g + c
+        const int base = imin(j0 - row, P - 1) + 4 * g;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c = 32 * kb + 8 * (i >> 2) + (i & 3);
+                x[kb][i] = fmaf(x[kb][i], ac, pos[base + c] + tv);
+            }
+    } else if (has_pos) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = j0 + 32 * kb + 4 * g + 8 * (i >> 2) + (i & 3);
+                x[kb][i] = fmaf(x[kb][i], ac, pos[imin(row > j ? row - j : j - row, P - 1)] + tv);
+            }
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[kb][i] = fmaf(x[kb][i], ac, tv);
     }
 }
 
@@ -405,8 +540,9 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     // bias only: the head's positional table and each stage's key timestamps
     // (at least 64 entries: one wave-load)
     constexpr int TSN = RAB ? (BN < 64 ? 64 : BN) : 1;
-    __shared__ float pos_lds[RAB ? HSTU_RAB_MAX_POS : 1];
+    __shared__ float pos_lds[RAB ? HSTU_RAB_MAX_POS + BN - 1 : 1];
     __shared__ __attribute__((aligned(16))) int32_t ts_lds[2][TSN];
+    __shared__ u32x4_t oct_lds[RAB ? kRabBinades : 1];  // time-bucket lookup per binade
 
     BlockPlan bp;
     if (!plan_block<BN, NW>(p, SPLIT, bp, red)) return;
@@ -463,24 +599,27 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
     // ---- relative attention bias set-up
     const bool has_pos = RAB && p.rab_pos != nullptr, has_time = RAB && p.rab_ts != nullptr;
-    constexpr float kDom = SOFTMAX ? kLog2e : 1.0f;  // the non-linearity's domain factor
-    float tt[HSTU_RAB_TIME_BUCKETS];
     int32_t t_row = 0;
     i32x4_t tsr = {};
-    const int pmax = has_pos ? p.rab_pos_len - 1 : 0;
+    const int wrow0 = bp.it.qt * C::BM + wave_u * 32;  // first row of this wave
     if constexpr (RAB) {
         if (has_pos) {
-            const float *ph = p.rab_pos + (int64_t)h * p.rab_pos_len;
-            for (int i = tid; i < p.rab_pos_len; i += C::NT) pos_lds[i] = ph[i] * kDom;
+            // The head's table, padded with its last entry up to P + BN - 1 entries
+            // (see rab_tile): whole 64-entry chunks go global -> LDS directly (they
+            // land with the first key tile, before the prologue's barrier), the
+            // rest (< 64 + BN - 1 <= NT entries) through registers, one per thread.
+            const int P = p.rab_pos_len, full = P / 64;
+            const float *ph = p.rab_pos + (int64_t)h * P;
+            const i32x4_t pr = make_rsrc_words(ph, (uint32_t)P * 4u);
+            const uint32_t pos_base = (uint32_t)(uintptr_t)(lds_void_t *)&pos_lds[0];
+            for (int c = wave_u; c < full; c += NW)
+                load_to_lds4(pr, pos_base + (uint32_t)c * 256u, (uint32_t)(c * 64 + lane) * 4u);
+            const int i = full * 64 + tid;
+            if (i < P + BN - 1) pos_lds[i] = ph[imin(i, P - 1)];
         }
-#pragma unroll
-        for (int k = 0; k < HSTU_RAB_TIME_BUCKETS; ++k) tt[k] = 0.0f;
         if (has_time) {
-#pragma unroll
-            for (int k = 0; k < HSTU_RAB_TIME_BUCKETS; ++k)
-                tt[k] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                                      int32_t, p.rab_time[h * HSTU_RAB_TIME_BUCKETS + k]))) *
-                        kDom;
+            if (tid < kRabBinades)
+                rab_binade_entry(tid, p.rab_time + h * HSTU_RAB_TIME_BUCKETS, &oct_lds[tid]);
             t_row = bp.row < s.S_q ? p.rab_ts[s.q0 + bp.row] : 0;
             tsr = make_rsrc_words(p.rab_ts + s.kv0, (uint32_t)s.S_kv * 4u);
         }
@@ -537,7 +676,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     float m_run = -INFINITY, l_run = 0.f;
     // with the bias the scores already carry alpha (rab_block)
     const float neg_alpha_log2e = RAB ? -kLog2e : -p.alpha * kLog2e;
-    const float sc_soft = RAB ? 1.0f : p.alpha * kLog2e;
+    const float sc_soft = RAB ? kLog2e : p.alpha * kLog2e;
     const uint8_t *lds0 = &lds[0][0];
 
     if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
@@ -588,12 +727,10 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
             // ---- mask + non-linearity; element i of block kb is key
             //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
-            if constexpr (RAB) {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-                    rab_block(sacc[kb], p.alpha * kDom, bp.row, j0 + kb * 32 + 4 * g, pos_lds, pmax,
-                              &ts_lds[buf][kb * 32 + 4 * g], t_row, tt, has_pos, has_time);
-            }
+            if constexpr (RAB)
+                rab_tile<C::NKB, BN>(sacc, p.alpha, bp.row, j0, g, wrow0, pos_lds, p.rab_pos_len,
+                                     ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
+                                     has_time, lane);
             if constexpr (!SOFTMAX) {
                 // p = x sigmoid(alpha x); the factor alpha of SiLU(alpha x) goes into the epilogue
                 if (wave_mask) {
