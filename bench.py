@@ -5,6 +5,7 @@ sequence and head): the mask, the non-linearity and both products run inside
 the timed kernels; inputs are resident in HBM before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--schedule S]
+                    [--rab none|pos|time|both]
 
 Prints one JSON line: effective TFLOP/s counting 2 * (hdim_qk + hdim_v) FLOPs
 per visible (b, h, i, j) pair, the roofline of the dominant kernel, and the CPU
@@ -28,6 +29,8 @@ METRIC = "HSTU fwd effective TFLOP/s (visible pairs) and % of bf16 MFMA peak, 1 
 DEFAULT_WORKLOAD = "jagged_silu_bf16_d128_causal_long"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
+RAB_SEED = 61          # bias inputs of the --rab runs
+RAB_POS_LEN = 2048     # positional table entries (the largest the kernel takes)
 KERNEL_SOURCES = [os.path.join(ROOT, "recsys_attention_amd", "csrc", f)
                   for f in ("hstu_fwd_kernels.hip", "hstu_plan.h", "hstu_params.h")]
 
@@ -49,6 +52,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
+    ap.add_argument("--rab", choices=("none", "pos", "time", "both"), default="none",
+                    help="relative attention bias terms (self-attention workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables cpu_baseline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -69,9 +74,10 @@ def copy_probe(mib: int):
                       "launches": 3}), flush=True)
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, rab=None):
     """The oracle, untuned, on whole sequences of the workload (all heads) until
-    about budget_s of wall time; returns TFLOP/s over the visible pairs done."""
+    about budget_s of wall time; returns TFLOP/s over the visible pairs done.
+    rab: the workload's bias inputs (workloads.RabInputs) or None."""
     import numpy as np
 
     import oracle
@@ -93,7 +99,13 @@ def cpu_baseline(w, budget_s: float):
             # keep the whole workload's default scale (it does not change the work)
             p.ga = np.array([1.0 / max(w.uih_q)], np.float64)
         t0 = time.perf_counter()
-        _, _, pairs = oracle.forward(p, w.q[q0:q1], w.k[k0:k1], w.v[k0:k1], lib=lib)
+        if rab is None:
+            _, _, pairs = oracle.forward(p, w.q[q0:q1], w.k[k0:k1], w.v[k0:k1], lib=lib)
+        else:
+            ts = None if rab.timestamps is None else rab.timestamps[q0:q1]
+            _, _, pairs = oracle.forward_rab(p, w.q[q0:q1], w.k[k0:k1], w.v[k0:k1], timestamps=ts,
+                                             time_table=rab.time_table, pos_table=rab.pos_table,
+                                             lib=lib)
         secs += time.perf_counter() - t0
         done_pairs += pairs
         seqs += 1
@@ -106,23 +118,27 @@ def cpu_baseline(w, budget_s: float):
                       f"({done_pairs} visible pairs, {secs:.1f} s, fp64 C loops)"}
 
 
-def algorithmic_bytes(w) -> int:
-    """q, k and v read once, o (and the softmax LSE) written once."""
+def algorithmic_bytes(w, rab=None) -> int:
+    """q, k and v read once, o (and the softmax LSE) written once; with the bias,
+    the timestamps and tables read once."""
     b = 2 * (w.total_q * w.nhead * (w.hdim_qk + w.hdim_v) + w.total_kv * w.nhead * (w.hdim_qk + w.hdim_v))
     if w.softmax:
         b += 4 * w.total_q * w.nhead
+    if rab is not None:
+        for a in (rab.timestamps, rab.time_table, rab.pos_table):
+            b += 0 if a is None else a.nbytes
     return b
 
 
-def roofline(w, splits, tflops, ms, traffic):
+def roofline(w, splits, tflops, ms, traffic, rab=None):
     """Roofline of the step's dominant kernel.  A workload with few query rows per
     key (the split-KV cross-attention one: ~72 FLOP per byte, far below the
     ~310 FLOP/B balance point of the chip) is bounded by HBM; then `achieved` is
     the algorithmic bytes over the step time, which also holds the combine pass."""
     peak = PEAK_TFLOPS[w.dtype]
-    flops_per_byte = (tflops * 1e12 * ms * 1e-3) / algorithmic_bytes(w)
+    flops_per_byte = (tflops * 1e12 * ms * 1e-3) / algorithmic_bytes(w, rab)
     if flops_per_byte < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
-        gbs = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+        gbs = algorithmic_bytes(w, rab) / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "covers": "whole step" + (f" (split kernel + combine, {splits} splits)" if splits > 1 else ""),
@@ -144,13 +160,20 @@ def main():
     import torch
 
     import workloads as W
-    from hip_runner import DeviceInputs
+    from hip_runner import DeviceInputs, rab_kwargs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = W.config(args.workload)
     splits = args.splits or w.num_splits
-    print(f"bench: {w.name}, {w.total_q} q tokens, splits={splits}", file=sys.stderr, flush=True)
+    label = w.name if args.rab == "none" else f"{w.name}+rab_{args.rab}"
+    print(f"bench: {label}, {w.total_q} q tokens, splits={splits}", file=sys.stderr, flush=True)
     dev = DeviceInputs(w)
+    rab = None
+    if args.rab != "none":
+        # bias inputs drawn once (seeded) and resident on the device like q/k/v
+        rab = W.rab_inputs(w, RAB_SEED, time=args.rab in ("time", "both"),
+                           pos_len=RAB_POS_LEN if args.rab in ("pos", "both") else None)
+        dev.kw.update(rab_kwargs(rab))
     stream = torch.cuda.current_stream()
     pairs = dev.count_pairs(schedule=args.schedule)
     flops = pairs * 2.0 * (w.hdim_qk + w.hdim_v)
@@ -175,7 +198,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
 
     traffic = None
-    tf = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    tf = os.path.join(ROOT, "profiles", f"traffic_{label}.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
         if rec.get("kernel_hash") == kernel_hash():
@@ -186,16 +209,16 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "nhead": w.nhead,
+        "config": {"workload": label, "batch": w.batch, "nhead": w.nhead,
                    "hdim_qk": w.hdim_qk, "hdim_v": w.hdim_v, "total_tokens": w.total_q,
                    "max_seqlen": w.max_seqlen_q, "visible_pairs": pairs,
                    "splits": splits, "schedule": args.schedule,
                    "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)},
-        "roofline": roofline(w, splits, tflops, ms, traffic),
+        "roofline": roofline(w, splits, tflops, ms, traffic, rab),
         "wall_s_timed": round(wall, 3),
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, rab)
     print(json.dumps(out), flush=True)
 
 
