@@ -20,6 +20,9 @@ Parity status (what pins each function, see tests/test_oracle_*.py):
                     bucket table (tests/golden/rab_time_buckets.json); the bias
                     as a whole by SDPA with an additive float mask (softmax) and
                     the dense SiLU product with the bias added (SiLU).
+  * HSTU layer (oracle/layer.py: f1 + SiLU + split, attention, norm * gate,
+                    f2 + residual) - pinned by an independent torch float64
+                    evaluation and the zero-gate / zero-f2 identities.
 """
 from __future__ import annotations
 

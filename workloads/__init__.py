@@ -309,3 +309,44 @@ def rab_inputs(w: Workload, seed: int, *, time=True, pos_len: Optional[int] = 64
     tt = rng.standard_normal((w.nhead, 11)).astype(np.float32) if time else None
     pt = rng.standard_normal((w.nhead, pos_len)).astype(np.float32) if pos_len else None
     return RabInputs(ts, tt, pt)
+
+
+# ----------------------------------------------------------------------------
+# HSTU layer inputs (the projections around the attention operator)
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LayerInputs:
+    d_model: int
+    x: np.ndarray          # [tokens, d_model] float32 (rounded to the dtype)
+    x_bits: np.ndarray
+    w1: np.ndarray         # [2 H dv + 2 H dqk, d_model] (rounded)
+    w1_bits: np.ndarray
+    b1: np.ndarray         # [2 H dv + 2 H dqk] float32
+    w2: np.ndarray         # [d_model, H dv] (rounded)
+    w2_bits: np.ndarray
+    b2: np.ndarray         # [d_model] float32
+    gamma: np.ndarray      # [H dv] float32
+    beta: np.ndarray       # [H dv] float32
+    eps: float = 1e-6
+
+
+def layer_inputs(w: Workload, d_model: int, seed: int) -> LayerInputs:
+    """Seeded inputs of one layer over workload w's sequences (its q/k/v are not
+    used: the layer makes them from X).  Draw order x -> w1 -> b1 -> w2 -> b2 ->
+    gamma -> beta from ``numpy.random.default_rng(seed)``.  X ~ N(0, 1); weights
+    N(0, 1/fan_in) (unit-variance pre-activations), rounded once to w.dtype like
+    X; biases N(0, 0.1^2), gamma 1 + N(0, 0.1^2), beta N(0, 0.1^2) in float32."""
+    rng = np.random.default_rng(seed)
+    H, dqk, dv = w.nhead, w.hdim_qk, w.hdim_v
+    n1 = 2 * H * (dv + dqk)
+    x, xb = round_to_dtype(rng.standard_normal((w.total_q, d_model)).astype(np.float32), w.dtype)
+    w1, w1b = round_to_dtype((rng.standard_normal((n1, d_model)) / np.sqrt(d_model)).astype(np.float32),
+                             w.dtype)
+    b1 = (0.1 * rng.standard_normal(n1)).astype(np.float32)
+    w2, w2b = round_to_dtype((rng.standard_normal((d_model, H * dv)) / np.sqrt(H * dv)).astype(np.float32),
+                             w.dtype)
+    b2 = (0.1 * rng.standard_normal(d_model)).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(H * dv)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(H * dv)).astype(np.float32)
+    return LayerInputs(d_model, x, xb, w1, w1b, b1, w2, w2b, b2, gamma, beta)
