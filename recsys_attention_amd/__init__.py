@@ -20,7 +20,8 @@ import torch
 from . import _abi
 
 __all__ = ["HstuGroup", "hstu_fwd", "hstu_fwd_splitkv", "hstu_count_visible_pairs",
-           "workspace_size", "group_max_uih", "is_available", "library_path"]
+           "workspace_size", "group_max_uih", "is_available", "library_path",
+           "hstu_linear", "hstu_norm_gate", "hstu_layer", "hstu_layer_workspace_size"]
 
 
 @dataclasses.dataclass
@@ -253,3 +254,175 @@ def hstu_count_visible_pairs(q, k, v, *, stream=None, **kw) -> int:
     _abi.check(lib.hstu_count_visible_pairs(ctypes.byref(c.args), ctypes.c_void_p(cnt.data_ptr()),
                                             c.stream(stream)))
     return int(cnt.item())
+
+
+# ------------------------------------------------------------- the HSTU layer
+# (include/hstu_layer.h: HSTU explainer, "The layer, line by line")
+
+_ACT = {"none": _abi.HSTU_ACT_NONE, "silu": _abi.HSTU_ACT_SILU}
+
+
+def _stream_ptr(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _rows2d(t: torch.Tensor, name: str):
+    if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D device tensor with contiguous rows")
+    return t.stride(0)
+
+
+def _f32vec(t: Optional[torch.Tensor], n: int, name: str):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous float32 device tensor of {n} elements")
+    return t.data_ptr()
+
+
+def hstu_linear(x, w, bias=None, *, activation="none", residual=None, out=None, stream=None):
+    """y = act(x w^T + bias) (+ residual): x [M, K] (rows may be strided), w [N, K]
+    contiguous (a torch Linear weight), bias float32 [N], residual [M, N]."""
+    lib = _abi.load()
+    dt = _dtype_code(x)
+    xs = _rows2d(x, "x")
+    if w.dtype != x.dtype or not w.is_cuda or not w.is_contiguous() or w.dim() != 2:
+        raise ValueError("w must be a contiguous 2-D device tensor of x's dtype")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w is [{N}, {w.shape[1]}], x has {K} features")
+    rs = 0
+    if residual is not None:
+        if residual.dtype != x.dtype or tuple(residual.shape) != (M, N):
+            raise ValueError(f"residual must be [{M}, {N}] of x's dtype")
+        rs = _rows2d(residual, "residual")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}] of x's dtype")
+    a = _abi.LinearArgsC(dtype=dt, rows=M, in_features=K, out_features=N, x=x.data_ptr(), x_stride=xs,
+                         w=w.data_ptr(), bias=_f32vec(bias, N, "bias"), activation=_ACT[activation],
+                         residual=_ptr(residual), residual_stride=rs, y=out.data_ptr(),
+                         y_stride=_rows2d(out, "out"))
+    _abi.check(lib.hstu_linear_fwd(ctypes.byref(a), _stream_ptr(x.device, stream)))
+    return out
+
+
+def hstu_norm_gate(a, u, gamma=None, beta=None, eps=1e-6, *, out=None, stream=None):
+    """(LayerNorm(a) * gamma + beta) * u over the last dim of the 2-D tensors a, u
+    (rows may be strided; out may be a)."""
+    lib = _abi.load()
+    dt = _dtype_code(a)
+    if u.dtype != a.dtype or u.shape != a.shape:
+        raise ValueError("u must match a's shape and dtype")
+    M, W_ = a.shape
+    if out is None:
+        out = torch.empty((M, W_), dtype=a.dtype, device=a.device)
+    if out.dtype != a.dtype or out.shape != a.shape:
+        raise ValueError("out must match a's shape and dtype")
+    args = _abi.NormGateArgsC(dtype=dt, rows=M, width=W_, a=a.data_ptr(), a_stride=_rows2d(a, "a"),
+                              u=u.data_ptr(), u_stride=_rows2d(u, "u"),
+                              gamma=_f32vec(gamma, W_, "gamma"), beta=_f32vec(beta, W_, "beta"),
+                              eps=float(eps), z=out.data_ptr(), z_stride=_rows2d(out, "out"))
+    _abi.check(lib.hstu_norm_gate_fwd(ctypes.byref(args), _stream_ptr(a.device, stream)))
+    return out
+
+
+class _LayerCall:
+    """The hstu_layer_args_t of one call plus the objects it points into."""
+
+    def __init__(self, x, w1, b1, w2, b2, *, nhead, hdim_qk, hdim_v, ln_gamma, ln_beta, ln_eps,
+                 seq_offsets, max_seqlen, batch, num_targets, causal, softmax, alpha, groups,
+                 schedule, rab_timestamps, rab_time, rab_pos, out):
+        dt = _dtype_code(x)
+        if not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [tokens, d_model] device tensor")
+        n, d_model = x.shape
+        H, dqk, dv = int(nhead), int(hdim_qk), int(hdim_v)
+        n1 = 2 * H * (dv + dqk)
+        for t, shape, name in ((w1, (n1, d_model), "w1"), (w2, (d_model, H * dv), "w2")):
+            if t.dtype != x.dtype or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be a contiguous {list(shape)} device tensor of x's dtype")
+        jagged = seq_offsets is not None
+        if jagged:
+            if seq_offsets.dtype != torch.int32 or not seq_offsets.is_cuda:
+                raise ValueError("seq_offsets must be an int32 device tensor")
+            if max_seqlen is None:
+                raise ValueError("jagged mode needs max_seqlen (an upper bound of the lengths)")
+            B, S = seq_offsets.numel() - 1, int(max_seqlen)
+        else:
+            if batch is None or n % int(batch):
+                raise ValueError("batched mode needs batch dividing the token count")
+            B, S = int(batch), n // int(batch)
+        if num_targets is not None and (num_targets.dtype != torch.int32 or not num_targets.is_cuda):
+            raise ValueError("num_targets must be an int32 device tensor")
+        _check_rab(rab_timestamps, rab_time, rab_pos, H, n)
+        if out is None:
+            out = torch.empty_like(x)
+        self.out = out
+        self.groups = _groups_c(groups)
+        self.keep = (x, w1, b1, w2, b2, ln_gamma, ln_beta, seq_offsets, num_targets, rab_timestamps,
+                     rab_time, rab_pos)
+        t = _abi.FwdArgsC()
+        t.dtype, t.batch, t.nhead, t.hdim_qk, t.hdim_v = dt, B, H, dqk, dv
+        t.jagged, t.cross = int(jagged), 0
+        t.seqlen_q = t.seqlen_kv = S
+        t.total_q = n
+        t.seq_offsets_q = _ptr(seq_offsets)
+        t.num_targets = _ptr(num_targets)
+        t.causal, t.softmax, t.alpha = int(bool(causal)), int(bool(softmax)), float(alpha)
+        t.num_groups = len(groups)
+        t.groups = ctypes.cast(self.groups, ctypes.POINTER(_abi.MaskGroupC))
+        t.schedule = int(schedule)
+        t.rab_timestamps, t.rab_time, t.rab_pos = _ptr(rab_timestamps), _ptr(rab_time), _ptr(rab_pos)
+        t.rab_pos_len = 0 if rab_pos is None else int(rab_pos.shape[-1])
+        a = _abi.LayerArgsC()
+        a.attn = t
+        a.d_model = d_model
+        a.x, a.w1, a.w2, a.out = x.data_ptr(), w1.data_ptr(), w2.data_ptr(), out.data_ptr()
+        a.b1 = _f32vec(b1, n1, "b1")
+        a.b2 = _f32vec(b2, d_model, "b2")
+        a.ln_gamma = _f32vec(ln_gamma, H * dv, "ln_gamma")
+        a.ln_beta = _f32vec(ln_beta, H * dv, "ln_beta")
+        a.ln_eps = float(ln_eps)
+        self.args = a
+        self.device = x.device
+
+
+def hstu_layer_workspace_size(x, w1, b1, w2, b2, **kw) -> int:
+    lib = _abi.load()
+    c = _LayerCall(x, w1, b1, w2, b2, **_layer_kw(kw))
+    return int(lib.hstu_layer_workspace_size(ctypes.byref(c.args)))
+
+
+def _layer_kw(kw):
+    d = dict(ln_gamma=None, ln_beta=None, ln_eps=1e-6, seq_offsets=None, max_seqlen=None, batch=None,
+             num_targets=None, causal=True, softmax=False, alpha=0.0, groups=(HstuGroup(),),
+             schedule=0, rab_timestamps=None, rab_time=None, rab_pos=None, out=None)
+    unknown = set(kw) - set(d) - {"nhead", "hdim_qk", "hdim_v"}
+    if unknown:
+        raise TypeError(f"unknown arguments {sorted(unknown)}")
+    d.update(kw)
+    return d
+
+
+def hstu_layer(x, w1, b1, w2, b2, *, workspace=None, stream=None, **kw):
+    """One HSTU layer: out = x + ((LayerNorm(A) * ln_gamma + ln_beta) * U) w2^T + b2 with
+    [U | V | Q | K] = SiLU(x w1^T + b1) and A the attention on Q, K, V.  Keywords:
+    nhead, hdim_qk, hdim_v (required); seq_offsets + max_seqlen (jagged) or batch;
+    the attention's mask, groups and rab_* as for hstu_fwd; ln_gamma, ln_beta, ln_eps.
+    The workspace (uint8 device tensor, hstu_layer_workspace_size bytes) is allocated
+    when not given."""
+    lib = _abi.load()
+    c = _LayerCall(x, w1, b1, w2, b2, **_layer_kw(kw))
+    need = int(lib.hstu_layer_workspace_size(ctypes.byref(c.args)))
+    if need == 0:
+        _abi.check(lib.hstu_layer_fwd(ctypes.byref(c.args), None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _abi.check(lib.hstu_layer_fwd(ctypes.byref(c.args), ctypes.c_void_p(workspace.data_ptr()),
+                                  workspace.numel(), _stream_ptr(x.device, stream)))
+    return c.out

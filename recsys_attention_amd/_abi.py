@@ -1,4 +1,4 @@
-"""ctypes mirror of include/hstu.h and the loader of libhstu.so.
+"""ctypes mirror of include/hstu.h and include/hstu_layer.h, and the loader of libhstu.so.
 
 Argument marshalling only: every step of the operator runs in the HIP library.
 If the library is not built this module raises; there is no fallback.
@@ -24,10 +24,14 @@ HSTU_ABI_VERSION = 2
 HSTU_RAB_TIME_BUCKETS = 11
 HSTU_RAB_MAX_POS = 2048
 
-# every symbol include/hstu.h declares
+HSTU_ACT_NONE = 0
+HSTU_ACT_SILU = 1
+
+# every symbol include/*.h declares
 EXPORTED = ("hstu_validate_args", "hstu_fwd_workspace_size", "hstu_fwd", "hstu_fwd_splitkv",
             "hstu_count_visible_pairs", "hstu_status_string", "hstu_last_error",
-            "hstu_abi_version")
+            "hstu_abi_version",
+            "hstu_linear_fwd", "hstu_norm_gate_fwd", "hstu_layer_workspace_size", "hstu_layer_fwd")
 
 
 class MaskGroupC(ctypes.Structure):
@@ -54,6 +58,29 @@ class FwdArgsC(ctypes.Structure):
                 ("schedule", ctypes.c_int32),
                 ("rab_timestamps", ctypes.c_void_p), ("rab_time", ctypes.c_void_p),
                 ("rab_pos", ctypes.c_void_p), ("rab_pos_len", ctypes.c_int32)]
+
+
+class LinearArgsC(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32),
+                ("x", ctypes.c_void_p), ("x_stride", ctypes.c_int64), ("w", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("activation", ctypes.c_int32),
+                ("residual", ctypes.c_void_p), ("residual_stride", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("y_stride", ctypes.c_int64)]
+
+
+class NormGateArgsC(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("rows", ctypes.c_int64), ("width", ctypes.c_int32),
+                ("a", ctypes.c_void_p), ("a_stride", ctypes.c_int64), ("u", ctypes.c_void_p),
+                ("u_stride", ctypes.c_int64), ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("z", ctypes.c_void_p), ("z_stride", ctypes.c_int64)]
+
+
+class LayerArgsC(ctypes.Structure):
+    _fields_ = [("attn", FwdArgsC), ("d_model", ctypes.c_int32), ("x", ctypes.c_void_p),
+                ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("ln_gamma", ctypes.c_void_p),
+                ("ln_beta", ctypes.c_void_p), ("ln_eps", ctypes.c_float), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("out", ctypes.c_void_p)]
 
 
 _lib = None
@@ -86,6 +113,15 @@ def load(path: str = LIB_PATH):
     lib.hstu_last_error.restype = ctypes.c_char_p
     lib.hstu_abi_version.argtypes = []
     lib.hstu_abi_version.restype = ctypes.c_int32
+    lib.hstu_linear_fwd.argtypes = [ctypes.POINTER(LinearArgsC), ctypes.c_void_p]
+    lib.hstu_linear_fwd.restype = ctypes.c_int
+    lib.hstu_norm_gate_fwd.argtypes = [ctypes.POINTER(NormGateArgsC), ctypes.c_void_p]
+    lib.hstu_norm_gate_fwd.restype = ctypes.c_int
+    lib.hstu_layer_workspace_size.argtypes = [ctypes.POINTER(LayerArgsC)]
+    lib.hstu_layer_workspace_size.restype = ctypes.c_size_t
+    lib.hstu_layer_fwd.argtypes = [ctypes.POINTER(LayerArgsC), ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p]
+    lib.hstu_layer_fwd.restype = ctypes.c_int
     if lib.hstu_abi_version() != HSTU_ABI_VERSION:
         raise RuntimeError("libhstu.so ABI version mismatch")
     _lib = lib

@@ -11,7 +11,8 @@ import sys
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 CSRC = os.path.join(_HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "hstu_fwd_kernels.hip"), os.path.join(CSRC, "hstu_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("hstu_fwd_kernels.hip", "hstu_layer_kernels.hip", "hstu_api.cpp",
+                                             "hstu_layer_api.cpp")]
 OUT = os.path.join(_HERE, "libhstu.so")
 
 HIPCC_FLAGS = [

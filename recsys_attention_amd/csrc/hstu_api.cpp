@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "hstu.h"
+#include "hstu_api_internal.h"
 #include "hstu_launch.h"
 #include "hstu_plan.h"
 
@@ -187,6 +188,24 @@ hstu_status_t hip_status(hipError_t e, const char *what) {
 }
 
 }  // namespace
+
+namespace hstu {
+namespace api {
+
+hstu_status_t fail(hstu_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+void clear_error() { g_last_error[0] = '\0'; }
+hstu_status_t validate_fwd(const hstu_fwd_args_t *a) { return validate(a); }
+hstu_status_t hip_status(hipError_t e, const char *what) { return ::hip_status(e, what); }
+int64_t rows_q(const hstu_fwd_args_t *a) { return ::rows_q(a); }
+
+}  // namespace api
+}  // namespace hstu
 
 extern "C" {
 

@@ -144,3 +144,45 @@ def compare_lse(lse: np.ndarray, ref: np.ndarray, what=""):
     assert np.array_equal(np.isneginf(lse), ninf), f"{what}: -inf rows differ"
     d = np.abs(lse[~ninf] - ref[~ninf])
     assert (d <= 1e-3 + 1e-4 * np.abs(ref[~ninf])).all(), f"{what}: lse err {d.max(initial=0)}"
+
+
+def bits_to_device(bits: np.ndarray, dtype: str, device="cuda"):
+    """Rounded bits (uint16) -> a device tensor of the dtype, same shape."""
+    return to_device(bits, dtype, device).view(bits.shape)
+
+
+def layer_kwargs(w, li, rab=None, device="cuda"):
+    """workloads.Workload + LayerInputs (+ RabInputs) -> (x, w1, b1, w2, b2, kwargs) for
+    recsys_attention_amd.hstu_layer."""
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+    x = bits_to_device(li.x_bits, w.dtype, device)
+    w1 = bits_to_device(li.w1_bits, w.dtype, device)
+    w2 = bits_to_device(li.w2_bits, w.dtype, device)
+    kw = dict(nhead=w.nhead, hdim_qk=w.hdim_qk, hdim_v=w.hdim_v, ln_gamma=f32(li.gamma),
+              ln_beta=f32(li.beta), ln_eps=li.eps,
+              num_targets=torch.tensor(w.targets, dtype=torch.int32, device=device),
+              causal=w.causal, softmax=w.softmax, alpha=w.alpha, groups=hip_groups(w))
+    if w.jagged:
+        kw.update(seq_offsets=torch.tensor(w.q_offsets, dtype=torch.int32, device=device),
+                  max_seqlen=w.max_seqlen_q)
+    else:
+        kw.update(batch=w.batch)
+    if rab is not None:
+        kw.update(rab_kwargs(rab, device))
+    return x, w1, f32(li.b1), w2, f32(li.b2), kw
+
+
+def compare_rounded(o: np.ndarray, ref: np.ndarray, dtype: str, what="", atol=1e-3):
+    """One rounding of an fp32 result to the dtype: |o - ref| <= 2^-8 |ref| (bf16;
+    2^-10 for fp16) + atol."""
+    o = np.asarray(o, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert o.shape == ref.shape, (o.shape, ref.shape)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    rt = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -10
+    err = np.abs(o - ref)
+    bound = atol + rt * np.abs(ref)
+    if err.size:
+        worst = np.unravel_index(np.argmax(err - bound), err.shape)
+        assert (err <= bound).all(), f"{what}: bound fails at {worst}: {o[worst]} vs {ref[worst]}"
+    return float(err.max(initial=0.0))
