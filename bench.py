@@ -148,6 +148,145 @@ def roofline(w, splits, tflops, ms, traffic, rab=None):
             "traffic_unit": "bytes per launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
 
 
+def layer_flops(w, d_model, pairs) -> float:
+    """f1 (2 n d_model N1) + the attention (2 (dqk + dv) per visible pair) + f2 (2 n H dv d_model)."""
+    n, H = w.total_q, w.nhead
+    n1 = 2 * H * (w.hdim_qk + w.hdim_v)
+    return 2.0 * n * d_model * n1 + pairs * 2.0 * (w.hdim_qk + w.hdim_v) + 2.0 * n * H * w.hdim_v * d_model
+
+
+def layer_cpu_baseline(w, d_model, li, rab, budget_s: float):
+    """The oracle layer (numpy float64 projections, the C attention oracle), untuned,
+    on whole sequences until about budget_s of wall time."""
+    import numpy as np
+
+    import oracle
+    import oracle.layer as OL
+    import workloads as W
+    lib = oracle.load()
+    flops, secs, seqs = 0.0, 0.0, 0
+    scale = 1.0 / max(max(w.uih_q), 1)
+    for b in range(w.batch):
+        sub = W.build("sample", dtype=w.dtype, batch=1, nhead=w.nhead, hdim_qk=w.hdim_qk,
+                      hdim_v=w.hdim_v, jagged=True, cross=False, causal=w.causal, softmax=w.softmax,
+                      alpha=w.alpha, groups=[W.MaskGroup(g.local_len, g.context_len, g.minfull_len,
+                                                         g.attn_scale or scale) for g in w.groups[:1]],
+                      uih_q=[w.uih_q[b]], targets=[w.targets[b]], materialize=False)
+        q0, q1 = w.q_offsets[b], w.q_offsets[b + 1]
+        r = W.RabInputs(None if rab.timestamps is None else rab.timestamps[q0:q1], rab.time_table,
+                        rab.pos_table)
+        p = oracle.problem_of(sub)
+        t0 = time.perf_counter()
+        OL.hstu_layer(p, li.x[q0:q1], li.w1, li.b1, li.w2, li.b2, li.gamma, li.beta, li.eps, rab=r)
+        secs += time.perf_counter() - t0
+        flops += layer_flops(sub, d_model, int(oracle.count_pairs(p, lib=lib).sum()) * w.nhead)
+        seqs += 1
+        if secs >= budget_s:
+            break
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib),
+            "kind": "oracle",
+            "sample": f"first {seqs} of {w.batch} sequences, whole layer, all {w.nhead} heads "
+                      f"({secs:.1f} s; numpy float64 projections, C float64 attention)"}
+
+
+def layer_main(args, torch):
+    """One step = one hstu_layer call over the whole workload.  A second timed loop
+    runs the same four kernels through their own entry points with HIP events
+    between them, for the per-kernel durations of the roofline."""
+    import recsys_attention_amd as hip
+    import workloads as W
+    from hip_runner import layer_kwargs
+
+    w, d_model, rab = W.layer_config(args.workload)
+    li = W.layer_inputs(w, d_model, W.LAYER_SEED)
+    x, w1, b1, w2, b2, kw = layer_kwargs(w, li, rab)
+    n, H, dqk, dv = w.total_q, w.nhead, w.hdim_qk, w.hdim_v
+    hv, hq, n1 = H * dv, H * dqk, 2 * H * (dv + dqk)
+    print(f"bench: {w.name}, {n} tokens, d_model {d_model}", file=sys.stderr, flush=True)
+    ws = torch.empty(hip.hstu_layer_workspace_size(x, w1, b1, w2, b2, **kw), dtype=torch.uint8,
+                     device=x.device)
+    out = torch.empty_like(x)
+    # views of the workspace as the layer lays it out: [U | V | Q | K] and the attention output
+    y1 = ws[:n * n1 * 2].view(x.dtype).view(n, n1)
+    off = (n * n1 * 2 + 255) // 256 * 256
+    ao = ws[off:off + n * hv * 2].view(x.dtype).view(n, hv)
+    attn_kw = {k: kw[k] for k in ("num_targets", "causal", "softmax", "alpha", "groups", "seq_offsets",
+                                  "rab_timestamps", "rab_time", "rab_pos")}
+    attn_kw["max_seqlen_q"] = kw["max_seqlen"]
+    q = y1[:, 2 * hv:2 * hv + hq].view(n, H, dqk)
+    k = y1[:, 2 * hv + hq:].view(n, H, dqk)
+    v = y1[:, hv:2 * hv].view(n, H, dv)
+    o = ao.view(n, H, dv)
+    pairs = hip.hstu_count_visible_pairs(q, k, v, **{a: b for a, b in attn_kw.items()
+                                                     if not a.startswith("rab_")})
+    flops = layer_flops(w, d_model, pairs)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        hip.hstu_layer(x, w1, b1, w2, b2, workspace=ws, out=out, **kw)
+
+    kernels = [
+        ("linear_f1_silu", lambda: hip.hstu_linear(x, w1, b1, activation="silu", out=y1),
+         2.0 * n * d_model * n1, 2 * (n * d_model + n1 * d_model + n * n1)),
+        ("hstu_fwd_kernel", lambda: hip.hstu_fwd(q, k, v, out=o, **attn_kw),
+         pairs * 2.0 * (dqk + dv), 2 * n * (2 * hq + 2 * hv)),
+        ("norm_gate", lambda: hip.hstu_norm_gate(ao, y1[:, :hv], kw["ln_gamma"], kw["ln_beta"],
+                                                 kw["ln_eps"], out=ao), 0.0, 2 * 3 * n * hv),
+        ("linear_f2_residual", lambda: hip.hstu_linear(ao, w2, b2, residual=x, out=out),
+         2.0 * n * hv * d_model, 2 * (n * hv + hv * d_model + 2 * n * d_model)),
+    ]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # per-kernel durations: events between the four launches of each step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        for i, (_, fn, _, _) in enumerate(kernels):
+            fn()
+            e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = []
+    for i, (name, _, kf, kb) in enumerate(kernels):
+        kms = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+        per.append({"kernel": name, "ms": round(kms, 4), "tflops": round(kf / (kms * 1e-3) / 1e12, 2),
+                    "gbs": round(kb / (kms * 1e-3) / 1e9, 1)})
+    dom = max(range(len(kernels)), key=lambda i: per[i]["ms"])
+    name, _, kf, kb = kernels[dom]
+    kms = per[dom]["ms"]
+    if kf / kb >= PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": per[dom]["tflops"], "peak": PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": round(per[dom]["tflops"] / PEAK_TFLOPS[w.dtype], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": per[dom]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(per[dom]["gbs"] / PEAK_HBM_GBS, 4)}
+    roof.update({"kernel": name, "traffic": None, "per_kernel": per})
+    tflops = flops / (ms * 1e-3) / 1e12
+    out_line = {
+        "metric": "HSTU layer fwd effective TFLOP/s (f1, attention over visible pairs, f2), 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "nhead": H, "hdim_qk": dqk, "hdim_v": dv,
+                   "d_model": d_model, "total_tokens": n, "visible_pairs": pairs, "rab": "both",
+                   "pct_of_bf16_peak": round(100.0 * tflops / PEAK_TFLOPS[w.dtype], 2)},
+        "roofline": roof,
+        "wall_s_timed": round(wall, 3),
+    }
+    if args.cpu_seconds > 0:
+        out_line["cpu_baseline"] = layer_cpu_baseline(w, d_model, li, rab, args.cpu_seconds)
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +302,9 @@ def main():
     from hip_runner import DeviceInputs, rab_kwargs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload in W.LAYER_NAMES:
+        layer_main(args, torch)
+        return
     w = W.config(args.workload)
     splits = args.splits or w.num_splits
     label = w.name if args.rab == "none" else f"{w.name}+rab_{args.rab}"

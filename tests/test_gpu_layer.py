@@ -119,3 +119,37 @@ def test_layer_edge_lengths():
                 cross=False, causal=True, softmax=False, alpha=0.0, groups=groups,
                 uih_q=[0, 0, 1, 0, 129, 3], targets=[0, 5, 0, 1, 2, 0], materialize=False)
     _layer_case(w, 128, 77, W.rab_inputs(w, 78, pos_len=16))
+
+
+def test_layer_named_workload_sampled_rows():
+    """The benchmark's layer workload at full size (83 302 tokens, d_model 512,
+    4 heads of 128, both bias terms) in the benchmark's launch, against the oracle
+    on sampled tokens: f1 over each sampled token's whole sequence, the attention
+    of the sampled rows one by one, then the gated norm, f2 and the residual."""
+    w, d_model, rab = W.layer_config("hstu_layer_bf16_d512_h4_causal_long")
+    li = W.layer_inputs(w, d_model, W.LAYER_SEED)
+    x, w1, b1, w2, b2, kw = layer_kwargs(w, li, rab)
+    got = _host(hip.hstu_layer(x, w1, b1, w2, b2, **kw))
+    H, dqk, dv = w.nhead, w.hdim_qk, w.hdim_v
+    scale = 1.0 / max(max(w.uih_q), 1)  # the whole call's default attn_scale
+    rng = np.random.default_rng(9)
+    for b in rng.choice(w.batch, 3, replace=False):
+        a, e = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+        rows = np.sort(rng.choice(e - a, 6, replace=False))
+        _log(f"sequence {b} ({e - a} tokens), rows {rows.tolist()}")
+        sub = W.build("seq", dtype=w.dtype, batch=1, nhead=H, hdim_qk=dqk, hdim_v=dv, jagged=True,
+                      cross=False, causal=True, softmax=False, alpha=0.0,
+                      groups=[W.MaskGroup(g.local_len, g.context_len, g.minfull_len, scale)
+                              for g in w.groups], uih_q=[w.uih_q[b]], targets=[w.targets[b]],
+                      materialize=False)
+        y = OL.silu(OL.linear(li.x[a:e], li.w1, li.b1))
+        u, v, q, k = OL.split_uvqk(y, H, dqk, dv)
+        rb = np.zeros(len(rows) * H, np.int32)
+        rh = np.tile(np.arange(H, dtype=np.int32), len(rows))
+        ri = np.repeat(rows, H).astype(np.int32)
+        o, _ = oracle.rows_rab(oracle.problem_of(sub), q, k, v, rb, rh, ri,
+                               timestamps=rab.timestamps[a:e], time_table=rab.time_table,
+                               pos_table=rab.pos_table)
+        z = OL.norm_gate(o.reshape(len(rows), H * dv), u[rows], li.gamma, li.beta, li.eps)
+        ref = li.x[a + rows].astype(np.float64) + OL.linear(z, li.w2, li.b2)
+        compare(got[a + rows], ref, w.dtype, f"sequence {b}")

@@ -350,3 +350,20 @@ def layer_inputs(w: Workload, d_model: int, seed: int) -> LayerInputs:
     gamma = (1.0 + 0.1 * rng.standard_normal(H * dv)).astype(np.float32)
     beta = (0.1 * rng.standard_normal(H * dv)).astype(np.float32)
     return LayerInputs(d_model, x, xb, w1, w1b, b1, w2, w2b, b2, gamma, beta)
+
+
+# the named HSTU layer workload: the long causal sequences with d_model 512 and
+# 4 heads of 128 (H * d = d_model, as in the explainer's d = 512 example), both
+# bias terms (positional table of 2048 entries)
+LAYER_NAMES = ("hstu_layer_bf16_d512_h4_causal_long",)
+LAYER_SEED = 2024
+LAYER_RAB_SEED = 2025
+
+
+def layer_config(name: str, seed: int = DEFAULT_SEED):
+    """(attention Workload without q/k/v, d_model, RabInputs) of a named layer workload."""
+    if name != "hstu_layer_bf16_d512_h4_causal_long":
+        raise KeyError(name)
+    w = config("jagged_silu_bf16_d128_causal_long", seed, materialize=False)
+    w.name, w.nhead = name, 4
+    return w, 512, rab_inputs(w, LAYER_RAB_SEED, pos_len=2048)
