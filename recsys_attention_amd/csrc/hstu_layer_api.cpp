@@ -15,8 +15,9 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// the linear kernel addresses one 128-row tile with 32-bit offsets
-constexpr int64_t kMaxStride = (int64_t)1 << 23;
+// the linear kernel addresses one tile of up to 256 rows with 32-bit offsets and
+// a 32-bit buffer range (256 rows x 2^22 elements x 2 bytes = 2^31)
+constexpr int64_t kMaxStride = (int64_t)1 << 22;
 
 hstu_status_t check_linear(const hstu_linear_args_t *a) {
     hstu::api::clear_error();
