@@ -14,8 +14,8 @@
 // consecutive columns per register group: the epilogue stores 8 bytes per lane
 // and group.  x and w tiles (64 k wide) move global -> LDS directly
 // (buffer_load_dwordx4 ... lds) into a two-stage ring; the 16-byte k-chunks of
-// each 128-byte row are XOR-swizzled by (row & 7) so the operand reads of eight
-// consecutive rows touch all 32 banks.  The epilogue goes through LDS so that
+// each 128-byte row are XOR-swizzled by (row >> 1) & 7 so the operand reads of
+// sixteen consecutive rows (one 16-lane group) touch all 64 banks.  The epilogue goes through LDS so that
 // every store instruction writes whole 128-byte row segments.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -142,9 +142,11 @@ __global__ __launch_bounds__(kNT, BM == 256 ? 1 : 2) void linear_kernel(LinearPa
     const i32x4_t wr = make_rsrc_words(p.w + (int64_t)n0 * p.K, (uint32_t)nrows * ks2);
 
     // DMA: wave-load c of wave w fills physical chunks c*256 + tid of a tile:
-    // row 32c + tid/8, position tid%8, which holds logical k-chunk (tid%8) ^ (row & 7)
+    // row 32c + tid/8, position tid%8, which holds logical k-chunk
+    // (tid%8) ^ ((row >> 1) & 7): the 16 rows of a 16-lane read group then cover
+    // all 64 banks (two rows per 256 bytes, eight distinct chunk positions)
     const int row_in = tid >> 3, pc = tid & 7;
-    const uint32_t chunk = (uint32_t)((pc ^ (row_in & 7)) * 16);
+    const uint32_t chunk = (uint32_t)((pc ^ ((row_in >> 1) & 7)) * 16);
     const uint32_t x_lane = (uint32_t)row_in * xs2 + chunk, w_lane = (uint32_t)row_in * ks2 + chunk;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] + (uint32_t)wave_u * 1024;
     auto issue = [&](int kt, int st) {
@@ -158,10 +160,10 @@ __global__ __launch_bounds__(kNT, BM == 256 ? 1 : 2) void linear_kernel(LinearPa
             load_to_lds(wr, dst + T::XBYTES + c * 4096, w_lane + (uint32_t)(32 * c) * ks2 + kb);
     };
 
-    // operand reads: row (block base) + r32, logical chunk 2kk + g, swizzled by r32 & 7
+    // operand reads: row (block base) + r32, logical chunk 2kk + g, swizzled by (r32 >> 1) & 7
     uint32_t off[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) off[kk] = (uint32_t)(r32 * 128 + (((2 * kk + g) ^ (r32 & 7)) * 16));
+    for (int kk = 0; kk < 4; ++kk) off[kk] = (uint32_t)(r32 * 128 + (((2 * kk + g) ^ ((r32 >> 1) & 7)) * 16));
 
     f32x16_t acc[T::NB][T::MB];
 #pragma unroll
@@ -240,6 +242,196 @@ __global__ __launch_bounds__(kNT, BM == 256 ? 1 : 2) void linear_kernel(LinearPa
         const int64_t m = m0 + wm * WR + r;
         const int n = n0 + wn * WC + ch * 8;
         if (m < p.M && n < p.N) *(u32x4_t *)(p.y + m * p.y_stride + n) = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    }
+}
+
+// ------------------------------------------------ persistent 256 x 256 linear
+//
+// For shapes with many output tiles (f1 of a layer): one work-group of 8 waves
+// per CU walks its share of 256 x 256 tiles.  Wave (wm, wn) of the 2 x 4 wave
+// grid owns 128 rows x 64 columns (4 x 2 MFMA blocks, 128 accumulators).  k-tiles
+// are 32 wide (64-byte rows, chunks XOR-swizzled by (row >> 2) & 3) and run
+// through a 4-stage LDS ring that continues across the work-group's tiles: the
+// loads of step s + 3 are issued at step s, so three steps (96 KB per CU) are in
+// flight and a tile's first loads overlap the previous tile's last steps and
+// epilogue.  Twice the output per loaded byte of the 128 x 128 tiles.  The tile
+// bookkeeping is incremental (no divisions per step).
+constexpr int kPBM = 256, kPBN = 256, kPBK = 32, kPNT = 512, kPStages = 4;
+constexpr int kPStage = (kPBM + kPBN) * kPBK * 2;  // 32 KB: x tile | w tile
+constexpr int kPStageOut = 32 * 128;              // per-wave epilogue staging (32 rows x 64 cols)
+constexpr int kPBiasSlots = 4;                    // bias of four consecutive tiles (1 KB each)
+static_assert(8 * kPStageOut == kPStage, "the epilogue stages through one ring stage");
+
+// LDS writes of a wave made visible to the wave's other lanes (one wave's LDS
+// instructions execute in order; this keeps the compiler from reordering them)
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int DT, bool SILU, bool RES>
+__global__ __launch_bounds__(kPNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void linear_persistent_kernel(
+    LinearParams p) {
+    using E = Elem<DT>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kPStages * kPStage + kPBiasSlots * 1024];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves: 128 rows x 64 columns each
+
+    // this work-group's tiles: T = blockIdx.x + i * gridDim.x (gridDim a multiple of
+    // 8, so every T of a work-group maps to its own XCD); the valid ones form a prefix
+    const int32_t G = gridDim.x, b0 = blockIdx.x;
+    const int32_t total = ((p.m_tiles + 7) / 8) * 8 * p.n_tiles;
+    auto tile_of = [&](int32_t i, int64_t &m0, int32_t &n0) {  // i-th tile of this work-group
+        const int32_t T = b0 + i * G, loc = T >> 3;
+        m0 = (int64_t)((loc / p.n_tiles) * 8 + (T & 7)) * kPBM;
+        n0 = (loc % p.n_tiles) * kPBN;
+    };
+    int32_t ntiles = 0;
+    for (int32_t T = b0; T < total && ((T >> 3) / p.n_tiles) * 8 + (T & 7) < p.m_tiles; T += G) ++ntiles;
+    if (ntiles == 0) return;
+    const int32_t KT = p.K / kPBK;
+    const int32_t steps = ntiles * KT;
+
+    const uint32_t xs2 = (uint32_t)p.x_stride * 2, ks2 = (uint32_t)p.K * 2;
+    // DMA: wave w loads x rows [32w, 32w + 32) and w rows [32w, 32w + 32) of a stage,
+    // two wave-loads of 16 rows each; lane -> row lane/4, position lane%4, which holds
+    // logical chunk (lane%4) ^ ((row >> 2) & 3): the 16 rows of a 16-lane read group
+    // then cover all 64 banks (four rows per 256 bytes, four distinct positions)
+    const int lrow = lane >> 2;
+    const uint32_t lchunk = (uint32_t)(((lane & 3) ^ ((lrow >> 2) & 3)) * 16);
+    const uint32_t ldsb = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0];
+    // the step being loaded: tile iss_i, k-tile iss_kt, with that tile's descriptors
+    int32_t iss_i = 0, iss_kt = 0;
+    i32x4_t xr, wr, br;
+    auto set_tile = [&]() {
+        int64_t m0;
+        int32_t n0;
+        tile_of(iss_i, m0, n0);
+        const int64_t mrows = p.M - m0 < kPBM ? p.M - m0 : kPBM;
+        const int32_t nrows = p.N - n0 < kPBN ? p.N - n0 : kPBN;
+        xr = make_rsrc_words(p.x + m0 * p.x_stride, (uint32_t)mrows * xs2);
+        wr = make_rsrc_words(p.w + (int64_t)n0 * p.K, (uint32_t)nrows * ks2);
+        br = make_rsrc_words((const void *)((uintptr_t)p.bias + 4u * (uint32_t)n0), (uint32_t)nrows * 4u);
+    };
+    set_tile();
+    auto issue = [&](int32_t s) {  // the loads of step s (= iss_i * KT + iss_kt) into stage s % 4
+        const uint32_t dst = ldsb + (uint32_t)((s & (kPStages - 1)) * kPStage) + (uint32_t)wave_u * 2048;
+        const uint32_t kb = (uint32_t)iss_kt * (kPBK * 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t row = (uint32_t)(32 * wave_u + 16 * h + lrow);
+            load_to_lds(xr, dst + h * 1024, row * xs2 + lchunk + kb);
+            load_to_lds(wr, dst + kPBM * kPBK * 2 + h * 1024, row * ks2 + lchunk + kb);
+        }
+        // the tile's 256 bias values, with its first k-tile, into bias slot i % 4 (the
+        // slot's previous tile finished its epilogue before this tile's loads began,
+        // three steps ahead of it, since a tile has at least one step)
+        if (iss_kt == 0 && wave_u == 0 && p.bias != nullptr)
+            load_to_lds(br, ldsb + kPStages * kPStage + (uint32_t)(iss_i & (kPBiasSlots - 1)) * 1024,
+                        (uint32_t)lane * 16u);
+        if (++iss_kt == KT) {
+            iss_kt = 0;
+            if (++iss_i < ntiles) set_tile();
+        }
+    };
+    // wait until the loads of step s + 1 have landed (those of s + 2, s + 3 may be in flight)
+    auto wait_next = [&](int32_t s) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int after = (s + 2 < steps) + (s + 3 < steps);
+        if (after == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (after == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    // operand reads: row (block base) + r32, logical chunk 2kk + g, swizzled by (r32 >> 2) & 3
+    uint32_t off[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) off[kk] = (uint32_t)(r32 * 64 + (((2 * kk + g) ^ ((r32 >> 2) & 3)) * 16));
+
+    f32x16_t acc[2][4];
+    for (int32_t s = 0; s < 3 && s < steps; ++s) issue(s);
+    wait_next(-1);
+    __syncthreads();
+    int32_t kt = 0, cur_i = 0;  // the step computed: tile cur_i, k-tile kt
+    for (int32_t s = 0; s < steps; ++s) {
+        if (kt == 0) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] = f32x16_t{};
+        }
+        if (s + 3 < steps) issue(s + 3);
+        const uint8_t *st = &lds[(s & (kPStages - 1)) * kPStage];
+        const uint8_t *xs = st + wm * 128 * 64;
+        const uint8_t *ws = st + kPBM * kPBK * 2 + wn * 64 * 64;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            u32x4_t xo[4], wo[2];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) xo[b] = *(const u32x4_t *)(xs + b * 32 * 64 + off[kk]);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) wo[b] = *(const u32x4_t *)(ws + b * 32 * 64 + off[kk]);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = E::mfma(wo[nb], xo[mb], acc[nb][mb]);
+        }
+        wait_next(s);
+        __syncthreads();
+        if (++kt != KT) continue;
+        kt = 0;
+
+        // epilogue of this tile, 32 rows (one m-block) at a time through the wave's
+        // 4 KB of the stage just consumed (refilled only after the barrier below):
+        // rows of 128 bytes, 16-byte chunks XOR-swizzled by row & 7.  The bias comes
+        // from LDS, so the epilogue issues no global load that would wait behind the
+        // in-flight tile loads and its own stores.
+        const float *bias = (const float *)&lds[kPStages * kPStage + (cur_i & (kPBiasSlots - 1)) * 1024] + wn * 64;
+        int64_t m0;
+        int32_t n0;
+        tile_of(cur_i++, m0, n0);
+        m0 += wm * 128;
+        n0 += wn * 64;
+        uint8_t *so = &lds[(s & (kPStages - 1)) * kPStage + wave * kPStageOut];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int64_t m = m0 + mb * 32 + r32;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int c = nb * 32 + 8 * i4 + 4 * g;  // column inside the wave's 64
+                    const int n = n0 + c;
+                    f32x4_t v = {acc[nb][mb][4 * i4], acc[nb][mb][4 * i4 + 1], acc[nb][mb][4 * i4 + 2],
+                                 acc[nb][mb][4 * i4 + 3]};
+                    if (p.bias != nullptr) v += *(const f32x4_t *)(bias + c);
+                    if constexpr (SILU) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = v[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * v[e]));
+                    }
+                    if constexpr (RES) {
+                        if (m < p.M && n < p.N) v += E::unpack4(*(const u32x2_t *)(p.res + m * p.r_stride + n));
+                    }
+                    const int chunk = (c >> 3) ^ (r32 & 7);
+                    *(u32x2_t *)(so + r32 * 128 + chunk * 16 + (c & 7) * 2) = E::pack4(v);
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int r = it * 8 + (lane >> 3), ch = lane & 7;
+                const u32x4_t val = *(const u32x4_t *)(so + r * 128 + ((ch ^ (r & 7)) * 16));
+                const int64_t mm = m0 + mb * 32 + r;
+                const int n = n0 + ch * 8;
+                if (mm < p.M && n < p.N) *(u32x4_t *)(p.y + mm * p.y_stride + n) = val;
+            }
+            wave_lds_sync();
+        }
+        __syncthreads();  // the stage is refilled from the next step on
     }
 }
 
@@ -330,11 +522,41 @@ static hipError_t launch_linear_tile(LinearParams p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// 128 x 128 tiles, two work-groups per CU (256 x 256 tiles, one work-group per CU
-// with 256 accumulators per lane, measured slower: nothing overlaps a work-group's
-// first load and its epilogue)
+template <int DT>
+static hipError_t launch_linear_persistent(LinearParams p, int cus, hipStream_t stream) {
+    p.m_tiles = (p.M + kPBM - 1) / kPBM;
+    p.n_tiles = (p.N + kPBN - 1) / kPBN;
+    const dim3 g((unsigned)((cus / 8) * 8)), b(kPNT);
+    if (p.act == 1) {
+        if (p.res != nullptr) hipLaunchKernelGGL((linear_persistent_kernel<DT, true, true>), g, b, 0, stream, p);
+        else hipLaunchKernelGGL((linear_persistent_kernel<DT, true, false>), g, b, 0, stream, p);
+    } else {
+        if (p.res != nullptr) hipLaunchKernelGGL((linear_persistent_kernel<DT, false, true>), g, b, 0, stream, p);
+        else hipLaunchKernelGGL((linear_persistent_kernel<DT, false, false>), g, b, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+// compute units of the current device (cached per device)
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Persistent 256 x 256 tiles when there are at least four per CU (and K is a
+// multiple of their 32-wide k-tiles), else 128 x 128 tiles, two work-groups per CU.
 template <int DT>
 static hipError_t launch_linear_dt(const LinearParams &p, hipStream_t stream) {
+    const int cus = device_cus();
+    const int64_t big = ((p.M + kPBM - 1) / kPBM) * ((p.N + kPBN - 1) / kPBN);
+    if (cus >= 8 && big >= 4 * (int64_t)cus && p.K % kPBK == 0) return launch_linear_persistent<DT>(p, cus, stream);
     return launch_linear_tile<DT, 128, 128>(p, stream);
 }
 
