@@ -241,7 +241,10 @@ __global__ __launch_bounds__(kNT, BM == 256 ? 1 : 2) void linear_kernel(LinearPa
         const u32x2_t lo = *(const u32x2_t *)src, hi = *(const u32x2_t *)(src + 8);
         const int64_t m = m0 + wm * WR + r;
         const int n = n0 + wn * WC + ch * 8;
-        if (m < p.M && n < p.N) *(u32x4_t *)(p.y + m * p.y_stride + n) = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        // non-temporal: y is not read again by this kernel, and allocating it in L2
+        // evicts the x rows the other column tiles of the XCD still need
+        if (m < p.M && n < p.N)
+            __builtin_nontemporal_store(u32x4_t{lo.x, lo.y, hi.x, hi.y}, (u32x4_t *)(p.y + m * p.y_stride + n));
     }
 }
 
@@ -427,7 +430,9 @@ __global__ __launch_bounds__(kPNT) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
                 const u32x4_t val = *(const u32x4_t *)(so + r * 128 + ((ch ^ (r & 7)) * 16));
                 const int64_t mm = m0 + mb * 32 + r;
                 const int n = n0 + ch * 8;
-                if (mm < p.M && n < p.N) *(u32x4_t *)(p.y + mm * p.y_stride + n) = val;
+                // non-temporal (as in linear_kernel): measured HBM reads of f1 on the
+                // layer workload 270 MB -> 104 MB (x and w are 87 MB)
+                if (mm < p.M && n < p.N) __builtin_nontemporal_store(val, (u32x4_t *)(p.y + mm * p.y_stride + n));
             }
             wave_lds_sync();
         }
