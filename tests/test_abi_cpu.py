@@ -151,3 +151,100 @@ def test_binding_raises_without_library(tmp_path):
             _abi.load(str(tmp_path / "missing.so"))
     finally:
         _abi._lib = saved
+
+
+# ----------------------------------------------------------- the layer entry points
+
+def _linear(**over):
+    a = _abi.LinearArgsC(dtype=_abi.HSTU_BF16, rows=1000, in_features=512, out_features=2048,
+                         x=0x100000, x_stride=0, w=0x200000, bias=0x300000,
+                         activation=_abi.HSTU_ACT_SILU, residual=None, residual_stride=0,
+                         y=0x400000, y_stride=0)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=5), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(rows=-1), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(in_features=96), _abi.HSTU_ERR_UNSUPPORTED),       # not a multiple of 64
+    (dict(out_features=12), _abi.HSTU_ERR_UNSUPPORTED),      # not a multiple of 8
+    (dict(activation=3), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(x=None), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(bias=0x300004), _abi.HSTU_ERR_INVALID_ARG),        # misaligned
+    (dict(x_stride=500), _abi.HSTU_ERR_INVALID_ARG),         # shorter than a row
+    (dict(x_stride=516), _abi.HSTU_ERR_INVALID_ARG),         # not a multiple of 8
+    (dict(x_stride=(1 << 22) + 8), _abi.HSTU_ERR_UNSUPPORTED),  # beyond the 32-bit tile range
+    (dict(residual=0x500000, residual_stride=100), _abi.HSTU_ERR_INVALID_ARG),
+])
+def test_linear_invalid_args_rejected(lib, over, status):
+    assert lib.hstu_linear_fwd(ctypes.byref(_linear(**over)), None) == status
+    assert lib.hstu_last_error()
+
+
+def test_linear_empty_is_a_no_op(lib):
+    assert lib.hstu_linear_fwd(ctypes.byref(_linear(rows=0)), None) == _abi.HSTU_OK
+
+
+def _norm(**over):
+    a = _abi.NormGateArgsC(dtype=_abi.HSTU_BF16, rows=10, width=512, a=0x100000, a_stride=0,
+                           u=0x200000, u_stride=2048, gamma=None, beta=None, eps=1e-6, z=0x100000,
+                           z_stride=0)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(width=4104), _abi.HSTU_ERR_UNSUPPORTED),
+    (dict(width=12), _abi.HSTU_ERR_UNSUPPORTED),
+    (dict(eps=0.0), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(u=None), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(z_stride=1024), _abi.HSTU_ERR_INVALID_ARG),        # in place with another stride
+    (dict(gamma=0x300008), _abi.HSTU_ERR_INVALID_ARG),
+])
+def test_norm_gate_invalid_args_rejected(lib, over, status):
+    assert lib.hstu_norm_gate_fwd(ctypes.byref(_norm(**over)), None) == status
+
+
+def _layer(attn, **over):
+    """A valid layer block around the attention block attn (which the caller keeps
+    alive: it owns the host group array the library reads)."""
+    a = _abi.LayerArgsC()
+    a.attn = attn  # jagged, 10 sequences, 4 heads of 128, 8038 tokens
+    a.d_model, a.x, a.w1, a.b1, a.w2, a.b2, a.out = 512, 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+    a.ln_eps = 1e-6
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_layer_workspace_size(lib):
+    attn = _args()
+    a = _layer(attn)
+    n, H, d = 8038, 4, 128
+    proj = (n * 2 * H * (d + d) * 2 + 255) // 256 * 256
+    att = (n * H * d * 2 + 255) // 256 * 256
+    assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == proj + att
+    assert lib.hstu_layer_fwd(ctypes.byref(a), None, 0, None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), proj + att - 1,
+                              None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700010), proj + att,
+                              None) == _abi.HSTU_ERR_WORKSPACE  # not 256-byte aligned
+
+
+@pytest.mark.parametrize("attn_over,over,status", [
+    (dict(cross=1, seq_offsets_kv=0x58000), {}, _abi.HSTU_ERR_UNSUPPORTED),
+    ({}, dict(d_model=100), _abi.HSTU_ERR_UNSUPPORTED),
+    ({}, dict(w2=None), _abi.HSTU_ERR_INVALID_ARG),
+    ({}, dict(ln_eps=-1.0), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(hdim_qk=80, hdim_v=80), {}, _abi.HSTU_ERR_UNSUPPORTED),
+    ({}, dict(b2=0x500004), _abi.HSTU_ERR_INVALID_ARG),
+])
+def test_layer_invalid_args_rejected(lib, attn_over, over, status):
+    attn = _args(**attn_over)
+    a = _layer(attn, **over)
+    assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == 0
+    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), 1 << 30, None) == status
