@@ -21,6 +21,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "hstu_layer_launch.h"
 
 namespace hstu {
@@ -448,12 +450,11 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// One wave per row: the row's W features (W = 8 * 64 * c for c chunks per lane
-// at most kMaxChunks) are held in registers, mean and variance in two passes.
-constexpr int kMaxChunks = 8;  // W <= 4096
-
-template <int DT>
+// One wave per row: the row's W features (up to CH 16-byte chunks per lane, W <=
+// 512 CH) are held in registers with the gate row, mean and variance in two passes.
+template <int DT, int CH>
 __global__ __launch_bounds__(256) void norm_gate_kernel(NormGateParams p) {
+    constexpr int kMaxChunks = CH;
     using E = Elem<DT>;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -462,12 +463,14 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(NormGateParams p) {
     const uint16_t *a = p.a + row * p.a_stride;
     const uint16_t *u = p.u + row * p.u_stride;
     f32x4_t v[kMaxChunks][2];
+    u32x4_t ub[kMaxChunks];  // the gate, loaded together with the row (one memory latency per row)
     float s = 0.0f;
 #pragma unroll
     for (int t = 0; t < kMaxChunks; ++t) {
         const int c = lane + 64 * t;
         if (c < nch) {
             const u32x4_t b = *(const u32x4_t *)(a + 8 * c);
+            ub[t] = *(const u32x4_t *)(u + 8 * c);
             v[t][0] = E::unpack4(u32x2_t{b.x, b.y});
             v[t][1] = E::unpack4(u32x2_t{b.z, b.w});
             s += (v[t][0].x + v[t][0].y + v[t][0].z + v[t][0].w) + (v[t][1].x + v[t][1].y + v[t][1].z + v[t][1].w);
@@ -492,7 +495,6 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(NormGateParams p) {
     for (int t = 0; t < kMaxChunks; ++t) {
         const int c = lane + 64 * t;
         if (c < nch) {
-            const u32x4_t ub = *(const u32x4_t *)(u + 8 * c);
             u32x2_t o[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(NormGateParams p) {
                 const int f = 8 * c + 4 * h;
                 if (p.gamma != nullptr) y *= *(const f32x4_t *)(p.gamma + f);
                 if (p.beta != nullptr) y += *(const f32x4_t *)(p.beta + f);
-                y *= E::unpack4(h ? u32x2_t{ub.z, ub.w} : u32x2_t{ub.x, ub.y});
+                y *= E::unpack4(h ? u32x2_t{ub[t].z, ub[t].w} : u32x2_t{ub[t].x, ub[t].y});
                 o[h] = E::pack4(y);
             }
             *(u32x4_t *)(z + 8 * c) = u32x4_t{o[0].x, o[0].y, o[1].x, o[1].y};
@@ -542,17 +544,18 @@ static hipError_t launch_linear_persistent(LinearParams p, int cus, hipStream_t 
     return hipGetLastError();
 }
 
-// compute units of the current device (cached per device)
+// compute units of the current device (cached per device; safe to call from
+// several host threads, which at worst query the attribute more than once)
 static int device_cus() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // Persistent 256 x 256 tiles when there are at least four per CU (and K is a
@@ -569,11 +572,20 @@ hipError_t launch_linear(const LinearParams &p, int dtype, hipStream_t stream) {
     return dtype == HSTU_BF16 ? launch_linear_dt<HSTU_BF16>(p, stream) : launch_linear_dt<HSTU_FP16>(p, stream);
 }
 
+template <int DT>
+static void launch_norm_gate_dt(const NormGateParams &p, dim3 g, dim3 b, hipStream_t stream) {
+    // registers sized to the row: chunks of 8 features per lane, 64 lanes
+    if (p.W <= 512) hipLaunchKernelGGL((norm_gate_kernel<DT, 1>), g, b, 0, stream, p);
+    else if (p.W <= 1024) hipLaunchKernelGGL((norm_gate_kernel<DT, 2>), g, b, 0, stream, p);
+    else if (p.W <= 2048) hipLaunchKernelGGL((norm_gate_kernel<DT, 4>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((norm_gate_kernel<DT, 8>), g, b, 0, stream, p);
+}
+
 hipError_t launch_norm_gate(const NormGateParams &p, int dtype, hipStream_t stream) {
     if (p.M <= 0) return hipSuccess;
     const dim3 g((unsigned)((p.M + 3) / 4)), b(256);
-    if (dtype == HSTU_BF16) hipLaunchKernelGGL((norm_gate_kernel<HSTU_BF16>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((norm_gate_kernel<HSTU_FP16>), g, b, 0, stream, p);
+    if (dtype == HSTU_BF16) launch_norm_gate_dt<HSTU_BF16>(p, g, b, stream);
+    else launch_norm_gate_dt<HSTU_FP16>(p, g, b, stream);
     return hipGetLastError();
 }
 

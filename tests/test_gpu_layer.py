@@ -70,7 +70,7 @@ def test_linear(case):
 
 @pytest.mark.parametrize("width,inplace,affine,dt", [(64, False, True, "bf16"), (512, True, True, "bf16"),
                                                      (520, False, False, "fp16"), (4096, True, True, "bf16"),
-                                                     (1024, False, True, "fp16")])
+                                                     (1024, False, True, "fp16"), (2048, False, True, "bf16")])
 def test_norm_gate(width, inplace, affine, dt):
     _log(f"norm_gate width={width} inplace={inplace} affine={affine} {dt}")
     rng = np.random.default_rng(width + 7 * inplace)
