@@ -35,6 +35,23 @@ KERNEL_SOURCES = [os.path.join(ROOT, "recsys_attention_amd", "csrc", f)
                   for f in ("hstu_fwd_kernels.hip", "hstu_plan.h", "hstu_params.h")]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (the oracle baseline runs there)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_info(torch) -> dict:
+    """Name, architecture and compute units of cuda:0 (as the runtime reports them)."""
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count}
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -113,7 +130,7 @@ def cpu_baseline(w, budget_s: float, rab=None):
             break
     flops = done_pairs * 2.0 * (w.hdim_qk + w.hdim_v)
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"first {seqs} of {w.batch} sequences, all {w.nhead} heads "
                       f"({done_pairs} visible pairs, {secs:.1f} s, fp64 C loops)"}
 
@@ -184,7 +201,7 @@ def layer_cpu_baseline(w, d_model, li, rab, budget_s: float):
         if secs >= budget_s:
             break
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"first {seqs} of {w.batch} sequences, whole layer, all {w.nhead} heads "
                       f"({secs:.1f} s; numpy float64 projections, C float64 attention)"}
 
@@ -280,6 +297,7 @@ def layer_main(args, torch):
                    "d_model": d_model, "total_tokens": n, "visible_pairs": pairs, "rab": "both",
                    "pct_of_bf16_peak": round(100.0 * tflops / PEAK_TFLOPS[w.dtype], 2)},
         "roofline": roof,
+        "device": device_info(torch),
         "wall_s_timed": round(wall, 3),
     }
     if args.cpu_seconds > 0:
@@ -357,6 +375,7 @@ def main():
                    "splits": splits, "schedule": args.schedule,
                    "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)},
         "roofline": roofline(w, splits, tflops, ms, traffic, rab),
+        "device": device_info(torch),
         "wall_s_timed": round(wall, 3),
     }
     if args.cpu_seconds > 0:
