@@ -118,20 +118,29 @@ hstu_status_t check_layer(const hstu_layer_args_t *a, LayerDims &d) {
         !aligned16(a->b1) || !aligned16(a->b2) || !aligned16(a->ln_gamma) || !aligned16(a->ln_beta))
         return fail(HSTU_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
     if (!(a->ln_eps > 0.0f) || !isfinite(a->ln_eps)) return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be positive");
-    // the attention block with placeholder (aligned, never dereferenced) buffers
+    d.hv = a->attn.nhead * a->attn.hdim_v;
+    d.hq = a->attn.nhead * a->attn.hdim_qk;
+    d.n1 = 2 * (d.hv + d.hq);
+    if (a->attn.nhead <= 0 || a->attn.hdim_v <= 0 || a->attn.hdim_qk <= 0)
+        return fail(HSTU_ERR_INVALID_ARG, "nhead and head dims must be positive");
+    if (d.hv > 4096) return fail(HSTU_ERR_UNSUPPORTED, "nhead * hdim_v = %d above 4096", d.hv);
+    if (d.n1 > (1 << 22) || a->d_model > (1 << 22)) return fail(HSTU_ERR_UNSUPPORTED, "layer too wide");
+    // the attention block exactly as hstu_layer_fwd will pass it (views of the
+    // projection with its token stride), on placeholder buffers that are aligned
+    // like the workspace's and never dereferenced: every check the attention would
+    // make runs here, before the first launch
     hstu_fwd_args_t t = a->attn;
-    t.q = t.k = t.v = (const void *)(uintptr_t)256;
-    t.o = (void *)(uintptr_t)256;
-    t.q_tok_stride = t.k_tok_stride = t.v_tok_stride = t.o_tok_stride = 0;
+    const uintptr_t base = 256;
+    t.v = (const void *)(base + 2 * (uintptr_t)d.hv);
+    t.q = (const void *)(base + 4 * (uintptr_t)d.hv);
+    t.k = (const void *)(base + 4 * (uintptr_t)d.hv + 2 * (uintptr_t)d.hq);
+    t.q_tok_stride = t.k_tok_stride = t.v_tok_stride = d.n1;
+    t.o = (void *)base;
+    t.o_tok_stride = d.hv;
     t.lse = nullptr;
     hstu_status_t st = hstu::api::validate_fwd(&t);
     if (st != HSTU_OK) return st;
     d.n = hstu::api::rows_q(&a->attn);
-    d.hv = a->attn.nhead * a->attn.hdim_v;
-    d.hq = a->attn.nhead * a->attn.hdim_qk;
-    d.n1 = 2 * (d.hv + d.hq);
-    if (d.hv > 4096) return fail(HSTU_ERR_UNSUPPORTED, "nhead * hdim_v = %d above 4096", d.hv);
-    if (d.n1 > (1 << 23) || a->d_model > (1 << 23)) return fail(HSTU_ERR_UNSUPPORTED, "layer too wide");
     return HSTU_OK;
 }
 

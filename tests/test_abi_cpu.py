@@ -248,3 +248,17 @@ def test_layer_invalid_args_rejected(lib, attn_over, over, status):
     a = _layer(attn, **over)
     assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == 0
     assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), 1 << 30, None) == status
+
+
+def test_layer_checks_the_attention_on_its_strided_views(lib):
+    """The layer's Q/K/V are views of the projection (token stride 2H(dqk+dv)), so a
+    sequence length the attention accepts on dense tensors can exceed its 32-bit
+    per-sequence range here; the layer must refuse before its first launch."""
+    attn = _args(seqlen_q=1_100_000, seqlen_kv=1_100_000, total_q=1_100_000)
+    dense = attn
+    assert lib.hstu_validate_args(ctypes.byref(dense)) == _abi.HSTU_OK  # dense: 1.1 GB per sequence
+    a = _layer(attn)
+    assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == 0
+    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), 1 << 40,
+                              None) == _abi.HSTU_ERR_UNSUPPORTED
+    assert b"4 GiB" in lib.hstu_last_error()
