@@ -114,6 +114,14 @@ struct BlockPlan {
     RowSpan span;
     TileList tiles;
     int32_t row;  // row inside the sequence owned by this lane
+    // every valid row of the work-group sees all of [full_lo, full_hi] (plus the
+    // context); full_lo > full_hi when some valid row's band is empty
+    int32_t full_lo, full_hi;
+    // key tile [j0, j0 + BN) is visible to every valid row of the work-group
+    __device__ __forceinline__ bool tile_full(int32_t j0, int32_t BN) const {
+        const int32_t j1 = j0 + BN;
+        return j1 <= s.Ck || (full_lo <= imax(j0, s.Ck) && j1 - 1 <= full_hi);
+    }
 };
 
 template <int BN, int NW>
@@ -127,21 +135,32 @@ __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, Bl
     if (r0 >= bp.s.S_q) return false;
     bp.row = r0 + wave * 32 + (lane & 31);
     bp.span = row_span(bp.s, p.causal, bp.row);
-    // union of the band parts over the work-group's rows
+    // union of the band parts over the work-group's rows, and their intersection
+    // over its valid rows (rows past the sequence do not constrain it)
     int32_t lo = wave_min(bp.span.lo);
     int32_t hi = wave_max(bp.span.hi);
+    int32_t flo = wave_max(bp.span.valid ? bp.span.lo : kEmptyHi);
+    int32_t fhi = wave_min(bp.span.valid ? bp.span.hi : kEmptyLo);
     if (lane == 0) {
-        red[2 * wave] = lo;
-        red[2 * wave + 1] = hi;
+        red[4 * wave] = lo;
+        red[4 * wave + 1] = hi;
+        red[4 * wave + 2] = flo;
+        red[4 * wave + 3] = fhi;
     }
     __syncthreads();
     lo = red[0];
     hi = red[1];
+    flo = red[2];
+    fhi = red[3];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-        lo = imin(lo, red[2 * w]);
-        hi = imax(hi, red[2 * w + 1]);
+        lo = imin(lo, red[4 * w]);
+        hi = imax(hi, red[4 * w + 1]);
+        flo = imax(flo, red[4 * w + 2]);
+        fhi = imin(fhi, red[4 * w + 3]);
     }
+    bp.full_lo = flo;
+    bp.full_hi = fhi;
     int32_t tb = 0, te = (bp.s.S_kv + BN - 1) / BN;
     if (split) split_range(bp.s.S_kv, BN, p.num_splits, bp.it.sp, &tb, &te);
     // rows r0.. exist (r0 < S_q), so the context tiles are needed
@@ -536,7 +555,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     using E = Elem<DT>;
     // two stages of [K tile | V tile]
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][C::STAGE];
-    __shared__ int32_t red[2 * NW];
+    __shared__ int32_t red[4 * NW];
     // bias only: the head's positional table and each stage's key timestamps
     // (at least 64 entries: one wave-load)
     constexpr int TSN = RAB ? (BN < 64 ? 64 : BN) : 1;
@@ -683,7 +702,8 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     wait_all_loads();
     __syncthreads();
 
-    for (int n = 0; n < ntiles; ++n) {
+    // one key tile through the generic body (any mask, any variant)
+    auto generic_step = [&](int n) {
         const int buf = n & 1;
         const bool has_next = n + 1 < ntiles;
         // after the last tile the loads fall past the sequence's buffer range: they
@@ -695,17 +715,6 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
         const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
 
-        if constexpr (!SOFTMAX && !RAB && D == 128 && DV == 128) {
-            if (wave_any && !wave_mask) {
-                silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc,
-                                          neg_alpha_log2e, [&](int idx) {
-                                              if (idx < LPT) issue_one(t_next, buf ^ 1, idx);
-                                          });
-                wait_all_loads_here();
-                __syncthreads();
-                continue;
-            }
-        }
         issue_loads(t_next, buf ^ 1);
         if (wave_any) {
             const uint8_t *stage = lds0 + buf * C::STAGE;
@@ -802,6 +811,30 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
         wait_all_loads_here();
         __syncthreads();
+    };
+    if constexpr (!SOFTMAX && !RAB && D == 128 && DV == 128) {
+        // Tiles visible to every valid row of the work-group run through the
+        // software-pipelined body, in a loop of their own; the others through the
+        // generic body.  (Choosing between the two bodies per tile inside one loop
+        // made the compiler copy the 64 output accumulators between two register
+        // sets on every tile.)
+        auto full_step = [&](int n) {
+            const int buf = n & 1;
+            const int t_next = n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
+            silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
+                                      [&](int idx) {
+                                          if (idx < LPT) issue_one(t_next, buf ^ 1, idx);
+                                      });
+            wait_all_loads_here();
+            __syncthreads();
+        };
+        int n = 0;
+        while (n < ntiles) {
+            for (; n < ntiles && !bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) generic_step(n);
+            for (; n < ntiles && bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) full_step(n);
+        }
+    } else {
+        for (int n = 0; n < ntiles; ++n) generic_step(n);
     }
 
     // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
@@ -943,7 +976,7 @@ __global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D
 // the same full-tile shortcut).
 template <int BN, int NW>
 __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
-    __shared__ int32_t red[2 * NW];
+    __shared__ int32_t red[4 * NW];
     BlockPlan bp;
     if (!plan_block<BN, NW>(p, false, bp, red)) return;
     const int lane = threadIdx.x & 63, g = lane >> 5;
