@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 2
+#define HSTU_ABI_VERSION 3
 #define HSTU_MAX_GROUPS 64
 #define HSTU_MAX_SPLITS 128
 #define HSTU_RAB_TIME_BUCKETS 11 /* time-gap buckets of the relative attention bias */
@@ -111,8 +111,12 @@ typedef struct {
     const hstu_mask_group_t *groups; /* host array [num_groups], read during the call only */
     float *lse; /* softmax only, device, NULL = not saved: batched [B][H][S_q], jagged [H][total_q];
                    natural log; -inf for a row that sees no key */
-    int32_t schedule; /* work order: 0 = default (2), 1 = q-tile levels heavy-first,
-                         2 = per-XCD sequence groups (each (b,h) kept on one XCD's L2) */
+    int32_t schedule; /* work order: 0 = library's choice (3 when the workspace holds the
+                         work counters, else 2), 1 = q-tile levels heavy-first, 2 = per-XCD
+                         sequence groups (each (b,h) kept on one XCD's L2), one work-group per
+                         q-tile; 3 = the order of 2 taken from per-XCD queues by a persistent
+                         grid (one resident set of work-groups, no launch gaps or tail of
+                         short work-groups; needs the workspace) */
     /* Relative attention bias (HSTU explainer, "The layer, line by line" (b) and "The
      * relative attention bias"); self-attention only (HSTU_ERR_UNSUPPORTED with cross).
      * Added to the score before the mask and the non-linearity:
@@ -130,18 +134,25 @@ typedef struct {
 /* Host-only argument check (no HIP call); also run by every entry point. */
 hstu_status_t hstu_validate_args(const hstu_fwd_args_t *args);
 
-/* Bytes of workspace hstu_fwd_splitkv needs for num_splits splits (0 for
- * num_splits == 1, and for hstu_fwd).  Returns 0 on invalid arguments. */
+/* Bytes of workspace for num_splits splits (num_splits == 1: hstu_fwd): the split-KV
+ * partial results, plus 256 bytes of work counters when args->schedule is 0 or 3.
+ * Returns 0 on invalid arguments. */
 size_t hstu_fwd_workspace_size(const hstu_fwd_args_t *args, int32_t num_splits);
 
-/* The forward operator: one fused kernel per call.  ws may be NULL. */
+/* The forward operator: one fused kernel per call (plus a one-work-group kernel that
+ * clears the work counters, for schedule 3).  ws may be NULL: then schedule 0 runs
+ * as 2, and schedule 3 fails with HSTU_ERR_WORKSPACE.  A workspace of at least
+ * hstu_fwd_workspace_size(args, 1) bytes, 16-byte aligned, is used by schedule 0
+ * and 3; calls that share a workspace must not overlap in time. */
 hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Split-KV forward (README "Split-KV"): the key axis of every sequence is cut into
  * num_splits contiguous chunks processed by separate work-groups, which write fp32
  * partial outputs (and LSEs for softmax) into ws; a second kernel combines them into
  * o (and lse).  The result equals hstu_fwd's up to fp32 reassociation.
- * 1 <= num_splits <= HSTU_MAX_SPLITS; ws_bytes >= hstu_fwd_workspace_size(). */
+ * 1 <= num_splits <= HSTU_MAX_SPLITS; ws_bytes >= the partial results' share of
+ * hstu_fwd_workspace_size() (without the 256 bytes of counters schedule 0 runs
+ * as 2; schedule 3 needs them). */
 hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, void *ws,
                                size_t ws_bytes, void *hip_stream);
 

@@ -196,21 +196,40 @@ def _result(call, return_lse):
 def hstu_fwd(q, k, v, *, seq_offsets=None, seq_offsets_kv=None, num_targets=None,
              max_seqlen_q=None, max_seqlen_kv=None, cross=False, causal=True, softmax=False,
              alpha=0.0, groups=(HstuGroup(),), return_lse=False, out=None, schedule=0,
-             rab_timestamps=None, rab_time=None, rab_pos=None, stream=None):
+             rab_timestamps=None, rab_time=None, rab_pos=None, workspace=None, stream=None):
     """HSTU attention forward.  Batched: q [B, S_q, H, Dqk], k [B, S_kv, H, Dqk],
     v [B, S_kv, H, Dv].  Jagged: q/k/v [total, H, D] with int32 seq_offsets [B+1]
     (device) and max_seqlen_q.  Returns o (and the LSE when return_lse).
     Relative attention bias (self-attention): rab_timestamps int32 [tokens of q]
     with rab_time float32 [H, 11] (time-gap buckets), rab_pos float32 [H, P]
-    (positional, indexed by min(|i - j|, P - 1))."""
+    (positional, indexed by min(|i - j|, P - 1)).
+    schedule 0 and 3 use a small workspace (uint8 device tensor of workspace_size(...,
+    num_splits=1) bytes) for the persistent schedule's work counters; it is allocated
+    when not given."""
     lib = _abi.load()
     c = _Call(q, k, v, seq_offsets=seq_offsets, seq_offsets_kv=seq_offsets_kv,
               num_targets=num_targets, max_seqlen_q=max_seqlen_q, max_seqlen_kv=max_seqlen_kv,
               cross=cross, causal=causal, softmax=softmax, alpha=alpha, groups=groups,
               return_lse=return_lse, out=out, schedule=schedule, rab_timestamps=rab_timestamps,
               rab_time=rab_time, rab_pos=rab_pos)
-    _abi.check(lib.hstu_fwd(ctypes.byref(c.args), None, 0, c.stream(stream)))
+    ws_ptr, ws_bytes = _workspace(lib, c, 1, workspace, q.device, stream)
+    _abi.check(lib.hstu_fwd(ctypes.byref(c.args), ws_ptr, ws_bytes, c.stream(stream)))
     return _result(c, return_lse)
+
+
+def _workspace(lib, c, num_splits, workspace, device, stream):
+    """(pointer, bytes) of the call's workspace, allocated on the call's stream when
+    not given and the call needs one."""
+    need = int(lib.hstu_fwd_workspace_size(ctypes.byref(c.args), int(num_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        if stream is not None:
+            # the allocation belongs to the current stream; the kernels run on `stream`
+            workspace.record_stream(stream)
+    if workspace is None:
+        return None, 0
+    c.keep_workspace = workspace
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
 def workspace_size(q, k, v, num_splits, **kw) -> int:
@@ -235,11 +254,7 @@ def hstu_fwd_splitkv(q, k, v, num_splits, *, workspace=None, stream=None, **kw):
     lib = _abi.load()
     d = _call_kw(kw)
     c = _Call(q, k, v, **d)
-    need = int(lib.hstu_fwd_workspace_size(ctypes.byref(c.args), int(num_splits)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _ptr(workspace) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(lib, c, num_splits, workspace, q.device, stream)
     _abi.check(lib.hstu_fwd_splitkv(ctypes.byref(c.args), int(num_splits), ws_ptr, ws_bytes,
                                     c.stream(stream)))
     return _result(c, d["return_lse"])

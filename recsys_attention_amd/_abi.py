@@ -20,7 +20,7 @@ HSTU_FP16 = 0
 HSTU_BF16 = 1
 HSTU_MAX_GROUPS = 64
 HSTU_MAX_SPLITS = 128
-HSTU_ABI_VERSION = 2
+HSTU_ABI_VERSION = 3
 HSTU_RAB_TIME_BUCKETS = 11
 HSTU_RAB_MAX_POS = 2048
 

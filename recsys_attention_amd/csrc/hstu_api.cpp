@@ -48,8 +48,8 @@ hstu_status_t validate(const hstu_fwd_args_t *a) {
     }
     for (int32_t f : {a->jagged, a->cross, a->causal, a->softmax})
         if (f != 0 && f != 1) return fail(HSTU_ERR_INVALID_ARG, "jagged/cross/causal/softmax must be 0 or 1");
-    if (a->schedule < 0 || a->schedule > 2)
-        return fail(HSTU_ERR_INVALID_ARG, "schedule %d not in 0..2", a->schedule);
+    if (a->schedule < 0 || a->schedule > 3)
+        return fail(HSTU_ERR_INVALID_ARG, "schedule %d not in 0..3", a->schedule);
     if (a->seqlen_q < 0 || a->seqlen_kv < 0)
         return fail(HSTU_ERR_INVALID_ARG, "negative seqlen (%d, %d)", a->seqlen_q, a->seqlen_kv);
     if (!a->jagged && !a->cross && a->seqlen_kv != a->seqlen_q)
@@ -168,12 +168,38 @@ void fill_params(const hstu_fwd_args_t *a, int32_t num_splits, hstu::KernelParam
     }
 }
 
-size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+// Workspace layout: split-KV partial outputs (256-byte aligned), their LSEs
+// (softmax), then, for the persistent schedule, the work counters.
+size_t partial_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     if (num_splits <= 1) return 0;
     const size_t rows = (size_t)rows_q(a) * (size_t)a->nhead * (size_t)num_splits;
     const size_t o_bytes = rows * (size_t)a->hdim_v * sizeof(float);
     const size_t lse_bytes = a->softmax ? rows * sizeof(float) : 0;
-    return ((o_bytes + 255) / 256) * 256 + lse_bytes;
+    return ((o_bytes + 255) / 256) * 256 + ((lse_bytes + 255) / 256) * 256;
+}
+bool wants_queue(const hstu_fwd_args_t *a) { return a->schedule == 0 || a->schedule == 3; }
+size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+    return partial_bytes(a, num_splits) + (wants_queue(a) ? hstu::kQueueBytes : 0);
+}
+
+// Schedule and work counters of one call: the persistent schedule (3) when it
+// is asked for, or when the schedule is left to the library (0) and the
+// workspace holds the counters; else schedule 2 (0) or the one asked for.
+hstu_status_t pick_schedule(const hstu_fwd_args_t *a, int32_t num_splits, void *ws, size_t ws_bytes,
+                            hstu::KernelParams &p) {
+    const size_t part = partial_bytes(a, num_splits);
+    const bool room = ws != nullptr && ws_bytes >= part + hstu::kQueueBytes && aligned16(ws);
+    if (a->schedule == 3 && !room)
+        return fail(HSTU_ERR_WORKSPACE, "schedule 3 needs a 16-byte aligned workspace of %zu bytes, %zu given",
+                    part + hstu::kQueueBytes, ws ? ws_bytes : (size_t)0);
+    if (wants_queue(a) && room) {
+        p.schedule = 3;
+        p.queue = (uint32_t *)((char *)ws + part);
+    } else {
+        p.schedule = a->schedule == 0 ? 2 : a->schedule;
+        p.queue = nullptr;
+    }
+    return HSTU_OK;
 }
 
 hstu_status_t check_grid(const hstu::KernelParams &p) {
@@ -217,13 +243,12 @@ size_t hstu_fwd_workspace_size(const hstu_fwd_args_t *args, int32_t num_splits) 
 }
 
 hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, void *hip_stream) {
-    (void)ws;
-    (void)ws_bytes;
     hstu_status_t st = validate(args);
     if (st != HSTU_OK) return st;
     hstu::KernelParams p;
     fill_params(args, 1, p);
     if ((st = check_grid(p)) != HSTU_OK) return st;
+    if ((st = pick_schedule(args, 1, ws, ws_bytes, p)) != HSTU_OK) return st;
     if (p.total_rows == 0 || p.B == 0) return HSTU_OK;
     return hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, false,
                                            (hipStream_t)hip_stream),
@@ -237,7 +262,7 @@ hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, 
     if (num_splits < 1 || num_splits > HSTU_MAX_SPLITS)
         return fail(HSTU_ERR_INVALID_ARG, "num_splits %d not in 1..%d", num_splits, HSTU_MAX_SPLITS);
     if (num_splits == 1) return hstu_fwd(args, ws, ws_bytes, hip_stream);
-    const size_t need = workspace_bytes(args, num_splits);
+    const size_t need = partial_bytes(args, num_splits);
     if (!ws || ws_bytes < need)
         return fail(HSTU_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     ws ? ws_bytes : (size_t)0);
@@ -245,6 +270,7 @@ hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, 
     hstu::KernelParams p;
     fill_params(args, num_splits, p);
     if ((st = check_grid(p)) != HSTU_OK) return st;
+    if ((st = pick_schedule(args, num_splits, ws, ws_bytes, p)) != HSTU_OK) return st;
     if (p.total_rows == 0 || p.B == 0) return HSTU_OK;
     const size_t rows = (size_t)p.total_rows * (size_t)p.H * (size_t)num_splits;
     p.part_o = (float *)ws;

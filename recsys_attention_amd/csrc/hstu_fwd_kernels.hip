@@ -25,6 +25,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "hstu_launch.h"
 #include "hstu_plan.h"
 
@@ -126,9 +128,9 @@ struct BlockPlan {
 
 template <int BN, int NW>
 __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, BlockPlan &bp,
-                                           int32_t *red) {
+                                           int32_t *red, int64_t w) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    bp.it = decode_work(p, blockIdx.x);
+    bp.it = decode_work(p, w);
     if (!bp.it.valid) return false;
     bp.s = seq_geom(p, bp.it.b);
     const int32_t r0 = bp.it.qt * (32 * NW);
@@ -562,329 +564,395 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     __shared__ float pos_lds[RAB ? HSTU_RAB_MAX_POS + BN - 1 : 1];
     __shared__ __attribute__((aligned(16))) int32_t ts_lds[2][TSN];
     __shared__ u32x4_t oct_lds[RAB ? kRabBinades : 1];  // time-bucket lookup per binade
+    __shared__ int32_t next_item[2];
 
-    BlockPlan bp;
-    if (!plan_block<BN, NW>(p, SPLIT, bp, red)) return;
-    const SeqGeom &s = bp.s;
-    const RowSpan &span = bp.span;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
-    const int h = bp.it.h;
-    const int ntiles = bp.tiles.count();
+    // Persistent schedule, work counters: the work-group's own queue is that of
+    // its XCD (work-group ids go to the 8 XCDs in turn).  Thread 0 reserves the
+    // next item from it when the current item starts its last key tile, so the
+    // atomic's latency hides behind that tile (reserving earlier would double
+    // the items in flight and with them the keys competing for the XCD's L2).
+    constexpr uint32_t kNone = 0xffffffffu;
+    const int xq = (int)(blockIdx.x % 8);
+    uint32_t reserved = kNone;
+    auto reserve_next = [&]() {
+        if (p.queue != nullptr && threadIdx.x == 0) reserved = atomicAdd(&p.queue[xq], 1u);
+    };
 
-    // Buffer descriptors over this (sequence, head): rows past the sequence read as 0.
-    const uint32_t qs2 = (uint32_t)p.q_stride * 2, ks2 = (uint32_t)p.k_stride * 2,
-                   vs2 = (uint32_t)p.v_stride * 2;
-    const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc((const uint16_t *)p.q + s.q0 * p.q_stride + h * D, (uint32_t)s.S_q * qs2);
-    const i32x4_t kr =
-        make_rsrc_words((const uint16_t *)p.k + s.kv0 * p.k_stride + h * D, (uint32_t)s.S_kv * ks2);
-    const i32x4_t vr =
-        make_rsrc_words((const uint16_t *)p.v + s.kv0 * p.v_stride + h * DV, (uint32_t)s.S_kv * vs2);
+    // One work item (sequence, head, q-tile, split) from plan to output.
+    auto run_item = [&](const KernelParams &p, int64_t w) __attribute__((always_inline)) {
+        BlockPlan bp;
+        if (!plan_block<BN, NW>(p, SPLIT, bp, red, w)) return;
+        const SeqGeom &s = bp.s;
+        const RowSpan &span = bp.span;
+        // the lane's constants are derived per item (an opaque copy of the thread
+        // id keeps the compiler from hoisting them out of the item loop)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+        const int h = bp.it.h;
+        const int ntiles = bp.tiles.count();
 
-    // ---- Q^T operand: lane holds d = 16*kk + 8*g .. +7 of its row
-    u32x4_t qreg[C::KSTEPS];
-#pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk)
-        qreg[kk] = buf_load16(qr, (uint32_t)bp.row * qs2 + (kk * 16 + g * 8) * 2);
+        // Buffer descriptors over this (sequence, head): rows past the sequence read as 0.
+        const uint32_t qs2 = (uint32_t)p.q_stride * 2, ks2 = (uint32_t)p.k_stride * 2,
+                       vs2 = (uint32_t)p.v_stride * 2;
+        const __amdgpu_buffer_rsrc_t qr =
+            make_rsrc((const uint16_t *)p.q + s.q0 * p.q_stride + h * D, (uint32_t)s.S_q * qs2);
+        const i32x4_t kr =
+            make_rsrc_words((const uint16_t *)p.k + s.kv0 * p.k_stride + h * D, (uint32_t)s.S_kv * ks2);
+        const i32x4_t vr =
+            make_rsrc_words((const uint16_t *)p.v + s.kv0 * p.v_stride + h * DV, (uint32_t)s.S_kv * vs2);
 
-    // ---- global -> LDS loads of key tile t into stage b.  Wave-load c of wave w
-    //      fills physical chunks [(4c + w) 64, +64); the chunk a lane lands on
-    //      decides which logical chunk (swizzle undone) it fetches.
-    //      Physical chunk (c NT + tid) is row (c NT + tid) / CPR, chunk (c NT + tid) %
-    //      CPR; the lane's byte offset is its row's offset plus the swizzled chunk.
-    //      With whole rows per wave-load (CPR divides NT) the part that grows with c
-    //      is uniform (it goes with the tile into the scalar part of the address),
-    //      and when RPC is a multiple of the swizzle period the per-lane parts of all
-    //      c coincide (one register each).
-    constexpr bool kRowsK = C::NT % C::CPR == 0, kRowsV = C::NT % C::CPRV == 0;
-    constexpr int RPC = kRowsK ? C::NT / C::CPR : 0, RPCV = kRowsV ? C::NT / C::CPRV : 0;
-    uint32_t k_lane[C::LOADS], v_lane[C::LOADS_V];
-#pragma unroll
-    for (int c = 0; c < C::LOADS; ++c) {
-        const int phys = kRowsK ? tid : c * C::NT + tid;
-        const int row = phys / C::CPR, pc = phys % C::CPR;
-        const int rsw = (RPC & kKSwz) == 0 ? row : c * RPC + row;
-        k_lane[c] = (uint32_t)row * ks2 + (uint32_t)(pc ^ (rsw & kKSwz)) * 16;
-    }
-#pragma unroll
-    for (int c = 0; c < C::LOADS_V; ++c) {
-        const int phys = kRowsV ? tid : c * C::NT + tid;
-        const int row = phys / C::CPRV, pc = phys % C::CPRV;
-        v_lane[c] = (uint32_t)row * vs2 + (uint32_t)(pc ^ (kVSwz * (row & 3))) * 16;
-    }
-    // LDS byte address of this wave's first landing slot (wave-uniform)
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] + (uint32_t)wave_u * 1024;
+        // ---- Q^T operand: lane holds d = 16*kk + 8*g .. +7 of its row
+        u32x4_t qreg[C::KSTEPS];
+    #pragma unroll
+        for (int kk = 0; kk < C::KSTEPS; ++kk)
+            qreg[kk] = buf_load16(qr, (uint32_t)bp.row * qs2 + (kk * 16 + g * 8) * 2);
 
-    // ---- relative attention bias set-up
-    const bool has_pos = RAB && p.rab_pos != nullptr, has_time = RAB && p.rab_ts != nullptr;
-    int32_t t_row = 0;
-    i32x4_t tsr = {};
-    const int wrow0 = bp.it.qt * C::BM + wave_u * 32;  // first row of this wave
-    if constexpr (RAB) {
-        if (has_pos) {
-            // The head's table, padded with its last entry up to P + BN - 1 entries
-            // (see rab_tile): whole 64-entry chunks go global -> LDS directly (they
-            // land with the first key tile, before the prologue's barrier), the
-            // rest (< 64 + BN - 1 <= NT entries) through registers, one per thread.
-            const int P = p.rab_pos_len, full = P / 64;
-            const float *ph = p.rab_pos + (int64_t)h * P;
-            const i32x4_t pr = make_rsrc_words(ph, (uint32_t)P * 4u);
-            const uint32_t pos_base = (uint32_t)(uintptr_t)(lds_void_t *)&pos_lds[0];
-            for (int c = wave_u; c < full; c += NW)
-                load_to_lds4(pr, pos_base + (uint32_t)c * 256u, (uint32_t)(c * 64 + lane) * 4u);
-            const int i = full * 64 + tid;
-            if (i < P + BN - 1) pos_lds[i] = ph[imin(i, P - 1)];
+        // ---- global -> LDS loads of key tile t into stage b.  Wave-load c of wave w
+        //      fills physical chunks [(4c + w) 64, +64); the chunk a lane lands on
+        //      decides which logical chunk (swizzle undone) it fetches.
+        //      Physical chunk (c NT + tid) is row (c NT + tid) / CPR, chunk (c NT + tid) %
+        //      CPR; the lane's byte offset is its row's offset plus the swizzled chunk.
+        //      With whole rows per wave-load (CPR divides NT) the part that grows with c
+        //      is uniform (it goes with the tile into the scalar part of the address),
+        //      and when RPC is a multiple of the swizzle period the per-lane parts of all
+        //      c coincide (one register each).
+        constexpr bool kRowsK = C::NT % C::CPR == 0, kRowsV = C::NT % C::CPRV == 0;
+        constexpr int RPC = kRowsK ? C::NT / C::CPR : 0, RPCV = kRowsV ? C::NT / C::CPRV : 0;
+        uint32_t k_lane[C::LOADS], v_lane[C::LOADS_V];
+    #pragma unroll
+        for (int c = 0; c < C::LOADS; ++c) {
+            const int phys = kRowsK ? tid : c * C::NT + tid;
+            const int row = phys / C::CPR, pc = phys % C::CPR;
+            const int rsw = (RPC & kKSwz) == 0 ? row : c * RPC + row;
+            k_lane[c] = (uint32_t)row * ks2 + (uint32_t)(pc ^ (rsw & kKSwz)) * 16;
         }
-        if (has_time) {
-            if (tid < kRabBinades)
-                rab_binade_entry(tid, p.rab_time + h * HSTU_RAB_TIME_BUCKETS, &oct_lds[tid]);
-            t_row = bp.row < s.S_q ? p.rab_ts[s.q0 + bp.row] : 0;
-            tsr = make_rsrc_words(p.rab_ts + s.kv0, (uint32_t)s.S_kv * 4u);
+    #pragma unroll
+        for (int c = 0; c < C::LOADS_V; ++c) {
+            const int phys = kRowsV ? tid : c * C::NT + tid;
+            const int row = phys / C::CPRV, pc = phys % C::CPRV;
+            v_lane[c] = (uint32_t)row * vs2 + (uint32_t)(pc ^ (kVSwz * (row & 3))) * 16;
         }
-    }
-    const uint32_t ts_base = (uint32_t)(uintptr_t)(lds_void_t *)&ts_lds[0][0];
-    // the key timestamps of tile t into stage b: wave w < TSN / 64 loads 64 of them
-    auto issue_ts = [&](int t, int b) {
+        // LDS byte address of this wave's first landing slot (wave-uniform)
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)&lds[0][0] + (uint32_t)wave_u * 1024;
+
+        // ---- relative attention bias set-up
+        const bool has_pos = RAB && p.rab_pos != nullptr, has_time = RAB && p.rab_ts != nullptr;
+        int32_t t_row = 0;
+        i32x4_t tsr = {};
+        const int wrow0 = bp.it.qt * C::BM + wave_u * 32;  // first row of this wave
         if constexpr (RAB) {
-            if (has_time && wave_u < TSN / 64)
-                load_to_lds4(tsr, ts_base + (uint32_t)(b * TSN + wave_u * 64) * 4u,
-                             (uint32_t)(t * BN + wave_u * 64 + lane) * 4u);
-        }
-    };
-    // load idx of key tile t into stage b: idx < LOADS are K chunks, the rest V
-    constexpr int LPT = C::LOADS + C::LOADS_V;  // loads per tile and wave
-    auto issue_one = [&](int t, int b, int idx) {
-        if (idx < C::LOADS) {
-            const int c = idx;
-            const uint32_t r = (uint32_t)(t * BN + c * RPC);  // uniform
-            load_to_lds(kr, lds_base + b * C::STAGE + c * NW * 1024, k_lane[c] + r * ks2);
-        } else {
-            const int c = idx - C::LOADS;
-            const uint32_t r = (uint32_t)(t * BN + c * RPCV);
-            load_to_lds(vr, lds_base + b * C::STAGE + C::TILE_BYTES + c * NW * 1024, v_lane[c] + r * vs2);
-        }
-    };
-    auto issue_loads = [&](int t, int b) {
-#pragma unroll
-        for (int idx = 0; idx < LPT; ++idx) issue_one(t, b, idx);
-        issue_ts(t, b);
-    };
-
-    // ---- per-lane LDS read addresses (stage 0; stage 1 adds 2 * TILE_BYTES)
-    // K operand of S^T = K Q^T: row 32kb + r32, logical chunk 2kk + g
-    // (the swizzle mixes the low log2(NKA)+1 chunk bits, so NKA k-steps get their own
-    //  lane offsets and later k-steps repeat them one swizzle period further on)
-    constexpr int NKA = kKSwz ? (kKSwz + 1) / 2 : 1, NVA = kVSwz == 4 ? 4 : (kVSwz == 2 ? 2 : 1);
-    uint32_t k_addr[NKA];
-#pragma unroll
-    for (int m = 0; m < NKA; ++m)
-        k_addr[m] = (uint32_t)(r32 * C::RB + (((2 * m + g) ^ (r32 & kKSwz)) * 16));
-    // V^T operand (transposed read): row K0 + 4g + (i/4), columns 32nb + 16hb + 4(i%4)
-    const int i16 = lane & 15, hb = (lane >> 4) & 1;
-    const int vy = kVSwz * ((i16 >> 2) & 3);
-    uint32_t v_addr[NVA];
-#pragma unroll
-    for (int b2 = 0; b2 < NVA; ++b2)
-        v_addr[b2] = (uint32_t)(C::TILE_BYTES + (4 * g + (i16 >> 2)) * C::RBV +
-                                (((4 * b2 + 2 * hb + ((i16 & 3) >> 1)) ^ vy) * 16) + (i16 & 1) * 8);
-
-    f32x16_t oacc[C::NDB];
-#pragma unroll
-    for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] = f32x16_t{};
-    float m_run = -INFINITY, l_run = 0.f;
-    // with the bias the scores already carry alpha (rab_block)
-    const float neg_alpha_log2e = RAB ? -kLog2e : -p.alpha * kLog2e;
-    const float sc_soft = RAB ? kLog2e : p.alpha * kLog2e;
-    const uint8_t *lds0 = &lds[0][0];
-
-    if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
-    wait_all_loads();
-    __syncthreads();
-
-    // one key tile through the generic body (any mask, any variant)
-    auto generic_step = [&](int n) {
-        const int buf = n & 1;
-        const bool has_next = n + 1 < ntiles;
-        // after the last tile the loads fall past the sequence's buffer range: they
-        // return zeros into the free stage without touching memory, so no load
-        // needs a branch
-        const int t_next = has_next ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
-        const int j0 = bp.tiles.at(n) * BN;
-        const int32_t st = tile_state(span, j0, j0 + BN);
-        const bool wave_any = __ballot(st != kTileEmpty) != 0;
-        const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
-
-        issue_loads(t_next, buf ^ 1);
-        if (wave_any) {
-            const uint8_t *stage = lds0 + buf * C::STAGE;
-            // scores and non-linearity at wave priority 1, P.V at 0 (as in the
-            // pipelined tile)
-            __builtin_amdgcn_s_setprio(1);
-            // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
-            f32x16_t sacc[C::NKB];
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16_t{};
-#pragma unroll
-            for (int kk = 0; kk < C::KSTEPS; ++kk) {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-                    const uint8_t *ka = stage + k_addr[kk % NKA] + kb * 32 * C::RB + (kk / NKA) * (NKA * 32);
-                    sacc[kb] = E::mfma(*(const u32x4_t *)ka, qreg[kk], sacc[kb]);
-                }
+            if (has_pos) {
+                // The head's table, padded with its last entry up to P + BN - 1 entries
+                // (see rab_tile): whole 64-entry chunks go global -> LDS directly (they
+                // land with the first key tile, before the prologue's barrier), the
+                // rest (< 64 + BN - 1 <= NT entries) through registers, one per thread.
+                const int P = p.rab_pos_len, full = P / 64;
+                const float *ph = p.rab_pos + (int64_t)h * P;
+                const i32x4_t pr = make_rsrc_words(ph, (uint32_t)P * 4u);
+                const uint32_t pos_base = (uint32_t)(uintptr_t)(lds_void_t *)&pos_lds[0];
+                for (int c = wave_u; c < full; c += NW)
+                    load_to_lds4(pr, pos_base + (uint32_t)c * 256u, (uint32_t)(c * 64 + lane) * 4u);
+                const int i = full * 64 + tid;
+                if (i < P + BN - 1) pos_lds[i] = ph[imin(i, P - 1)];
             }
-
-            // ---- mask + non-linearity; element i of block kb is key
-            //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
-            if constexpr (RAB)
-                rab_tile<C::NKB, BN>(sacc, p.alpha, bp.row, j0, g, wrow0, pos_lds, p.rab_pos_len,
-                                     ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
-                                     has_time, lane);
-            if constexpr (!SOFTMAX) {
-                // p = x sigmoid(alpha x); the factor alpha of SiLU(alpha x) goes into the epilogue
-                if (wave_mask) {
-#pragma unroll
-                    for (int kb = 0; kb < C::NKB; ++kb)
-                        silu_block<true>(sacc[kb], neg_alpha_log2e, span, j0 + kb * 32 + 4 * g);
-                } else {
-#pragma unroll
-                    for (int kb = 0; kb < C::NKB; ++kb)
-                        silu_block<false>(sacc[kb], neg_alpha_log2e, span, 0);
-                }
+            if (has_time) {
+                if (tid < kRabBinades)
+                    rab_binade_entry(tid, p.rab_time + h * HSTU_RAB_TIME_BUCKETS, &oct_lds[tid]);
+                t_row = bp.row < s.S_q ? p.rab_ts[s.q0 + bp.row] : 0;
+                tsr = make_rsrc_words(p.rab_ts + s.kv0, (uint32_t)s.S_kv * 4u);
+            }
+        }
+        const uint32_t ts_base = (uint32_t)(uintptr_t)(lds_void_t *)&ts_lds[0][0];
+        // the key timestamps of tile t into stage b: wave w < TSN / 64 loads 64 of them
+        auto issue_ts = [&](int t, int b) {
+            if constexpr (RAB) {
+                if (has_time && wave_u < TSN / 64)
+                    load_to_lds4(tsr, ts_base + (uint32_t)(b * TSN + wave_u * 64) * 4u,
+                                 (uint32_t)(t * BN + wave_u * 64 + lane) * 4u);
+            }
+        };
+        // load idx of key tile t into stage b: idx < LOADS are K chunks, the rest V
+        constexpr int LPT = C::LOADS + C::LOADS_V;  // loads per tile and wave
+        auto issue_one = [&](int t, int b, int idx) {
+            if (idx < C::LOADS) {
+                const int c = idx;
+                const uint32_t r = (uint32_t)(t * BN + c * RPC);  // uniform
+                load_to_lds(kr, lds_base + b * C::STAGE + c * NW * 1024, k_lane[c] + r * ks2);
             } else {
-                float mx = -INFINITY;
-                if (wave_mask) {
-#pragma unroll
-                    for (int kb = 0; kb < C::NKB; ++kb)
-                        mx = fmaxf(mx, scale_block<true>(sacc[kb], sc_soft, span, j0 + kb * 32 + 4 * g));
-                } else {
-#pragma unroll
-                    for (int kb = 0; kb < C::NKB; ++kb)
-                        mx = fmaxf(mx, scale_block<false>(sacc[kb], sc_soft, span, 0));
-                }
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run, mx);
-                const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-                const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-                if (__ballot(corr != 1.0f) != 0) {
-                    l_run *= corr;
-#pragma unroll
-                    for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] *= corr;
-                }
-                m_run = m_new;
-                float lsum = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(sacc[kb][i] - m_use);
-                        lsum += e;
-                        sacc[kb][i] = e;
-                    }
-                }
-                l_run += lsum;
+                const int c = idx - C::LOADS;
+                const uint32_t r = (uint32_t)(t * BN + c * RPCV);
+                load_to_lds(vr, lds_base + b * C::STAGE + C::TILE_BYTES + c * NW * 1024, v_lane[c] + r * vs2);
             }
+        };
+        auto issue_loads = [&](int t, int b) {
+    #pragma unroll
+            for (int idx = 0; idx < LPT; ++idx) issue_one(t, b, idx);
+            issue_ts(t, b);
+        };
 
-            __builtin_amdgcn_s_setprio(0);
-            // ---- O^T += V^T P^T; MFMA step (kb, t2) covers keys
-            //      32kb + 16t2 + {4g..4g+3, 8+4g..8+4g+3} in both operands
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    const int i0 = 8 * t2;
-                    const u32x4_t pb = {E::pack2(sacc[kb][i0 + 0], sacc[kb][i0 + 1]),
-                                        E::pack2(sacc[kb][i0 + 2], sacc[kb][i0 + 3]),
-                                        E::pack2(sacc[kb][i0 + 4], sacc[kb][i0 + 5]),
-                                        E::pack2(sacc[kb][i0 + 6], sacc[kb][i0 + 7])};
-                    const int key0 = kb * 32 + 16 * t2;
-#pragma unroll
-                    for (int nb = 0; nb < C::NDB; ++nb) {
-                        const uint8_t *va = stage + v_addr[nb % NVA] + key0 * C::RBV + (nb / NVA) * (NVA * 64);
-                        const u32x2_t a0 = lds_read_tr16(va);
-                        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RBV);
-                        oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb, oacc[nb]);
-                    }
-                }
-            }
-        }
+        // ---- per-lane LDS read addresses (stage 0; stage 1 adds 2 * TILE_BYTES)
+        // K operand of S^T = K Q^T: row 32kb + r32, logical chunk 2kk + g
+        // (the swizzle mixes the low log2(NKA)+1 chunk bits, so NKA k-steps get their own
+        //  lane offsets and later k-steps repeat them one swizzle period further on)
+        constexpr int NKA = kKSwz ? (kKSwz + 1) / 2 : 1, NVA = kVSwz == 4 ? 4 : (kVSwz == 2 ? 2 : 1);
+        uint32_t k_addr[NKA];
+    #pragma unroll
+        for (int m = 0; m < NKA; ++m)
+            k_addr[m] = (uint32_t)(r32 * C::RB + (((2 * m + g) ^ (r32 & kKSwz)) * 16));
+        // V^T operand (transposed read): row K0 + 4g + (i/4), columns 32nb + 16hb + 4(i%4)
+        const int i16 = lane & 15, hb = (lane >> 4) & 1;
+        const int vy = kVSwz * ((i16 >> 2) & 3);
+        uint32_t v_addr[NVA];
+    #pragma unroll
+        for (int b2 = 0; b2 < NVA; ++b2)
+            v_addr[b2] = (uint32_t)(C::TILE_BYTES + (4 * g + (i16 >> 2)) * C::RBV +
+                                    (((4 * b2 + 2 * hb + ((i16 & 3) >> 1)) ^ vy) * 16) + (i16 & 1) * 8);
 
-        wait_all_loads_here();
+        f32x16_t oacc[C::NDB];
+    #pragma unroll
+        for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] = f32x16_t{};
+        float m_run = -INFINITY, l_run = 0.f;
+        // with the bias the scores already carry alpha (rab_block)
+        const float neg_alpha_log2e = RAB ? -kLog2e : -p.alpha * kLog2e;
+        const float sc_soft = RAB ? kLog2e : p.alpha * kLog2e;
+        const uint8_t *lds0 = &lds[0][0];
+
+        if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
+        wait_all_loads();
         __syncthreads();
-    };
-    if constexpr (!SOFTMAX && !RAB && D == 128 && DV == 128) {
-        // Tiles visible to every valid row of the work-group run through the
-        // software-pipelined body, in a loop of their own; the others through the
-        // generic body.  (Choosing between the two bodies per tile inside one loop
-        // made the compiler copy the 64 output accumulators between two register
-        // sets on every tile.)
-        auto full_step = [&](int n) {
+
+        // one key tile through the generic body (any mask, any variant)
+        auto generic_step = [&](int n) {
+            if (n == ntiles - 1) reserve_next();
             const int buf = n & 1;
-            const int t_next = n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
-            silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
-                                      [&](int idx) {
-                                          if (idx < LPT) issue_one(t_next, buf ^ 1, idx);
-                                      });
+            const bool has_next = n + 1 < ntiles;
+            // after the last tile the loads fall past the sequence's buffer range: they
+            // return zeros into the free stage without touching memory, so no load
+            // needs a branch
+            const int t_next = has_next ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
+            const int j0 = bp.tiles.at(n) * BN;
+            const int32_t st = tile_state(span, j0, j0 + BN);
+            const bool wave_any = __ballot(st != kTileEmpty) != 0;
+            const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
+
+            issue_loads(t_next, buf ^ 1);
+            if (wave_any) {
+                const uint8_t *stage = lds0 + buf * C::STAGE;
+                // scores and non-linearity at wave priority 1, P.V at 0 (as in the
+                // pipelined tile)
+                __builtin_amdgcn_s_setprio(1);
+                // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
+                f32x16_t sacc[C::NKB];
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16_t{};
+    #pragma unroll
+                for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    #pragma unroll
+                    for (int kb = 0; kb < C::NKB; ++kb) {
+                        const uint8_t *ka = stage + k_addr[kk % NKA] + kb * 32 * C::RB + (kk / NKA) * (NKA * 32);
+                        sacc[kb] = E::mfma(*(const u32x4_t *)ka, qreg[kk], sacc[kb]);
+                    }
+                }
+
+                // ---- mask + non-linearity; element i of block kb is key
+                //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
+                if constexpr (RAB)
+                    rab_tile<C::NKB, BN>(sacc, p.alpha, bp.row, j0, g, wrow0, pos_lds, p.rab_pos_len,
+                                         ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
+                                         has_time, lane);
+                if constexpr (!SOFTMAX) {
+                    // p = x sigmoid(alpha x); the factor alpha of SiLU(alpha x) goes into the epilogue
+                    if (wave_mask) {
+    #pragma unroll
+                        for (int kb = 0; kb < C::NKB; ++kb)
+                            silu_block<true>(sacc[kb], neg_alpha_log2e, span, j0 + kb * 32 + 4 * g);
+                    } else {
+    #pragma unroll
+                        for (int kb = 0; kb < C::NKB; ++kb)
+                            silu_block<false>(sacc[kb], neg_alpha_log2e, span, 0);
+                    }
+                } else {
+                    float mx = -INFINITY;
+                    if (wave_mask) {
+    #pragma unroll
+                        for (int kb = 0; kb < C::NKB; ++kb)
+                            mx = fmaxf(mx, scale_block<true>(sacc[kb], sc_soft, span, j0 + kb * 32 + 4 * g));
+                    } else {
+    #pragma unroll
+                        for (int kb = 0; kb < C::NKB; ++kb)
+                            mx = fmaxf(mx, scale_block<false>(sacc[kb], sc_soft, span, 0));
+                    }
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    const float m_new = fmaxf(m_run, mx);
+                    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+                    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+                    if (__ballot(corr != 1.0f) != 0) {
+                        l_run *= corr;
+    #pragma unroll
+                        for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] *= corr;
+                    }
+                    m_run = m_new;
+                    float lsum = 0.f;
+    #pragma unroll
+                    for (int kb = 0; kb < C::NKB; ++kb) {
+    #pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const float e = __builtin_amdgcn_exp2f(sacc[kb][i] - m_use);
+                            lsum += e;
+                            sacc[kb][i] = e;
+                        }
+                    }
+                    l_run += lsum;
+                }
+
+                __builtin_amdgcn_s_setprio(0);
+                // ---- O^T += V^T P^T; MFMA step (kb, t2) covers keys
+                //      32kb + 16t2 + {4g..4g+3, 8+4g..8+4g+3} in both operands
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) {
+    #pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const int i0 = 8 * t2;
+                        const u32x4_t pb = {E::pack2(sacc[kb][i0 + 0], sacc[kb][i0 + 1]),
+                                            E::pack2(sacc[kb][i0 + 2], sacc[kb][i0 + 3]),
+                                            E::pack2(sacc[kb][i0 + 4], sacc[kb][i0 + 5]),
+                                            E::pack2(sacc[kb][i0 + 6], sacc[kb][i0 + 7])};
+                        const int key0 = kb * 32 + 16 * t2;
+    #pragma unroll
+                        for (int nb = 0; nb < C::NDB; ++nb) {
+                            const uint8_t *va = stage + v_addr[nb % NVA] + key0 * C::RBV + (nb / NVA) * (NVA * 64);
+                            const u32x2_t a0 = lds_read_tr16(va);
+                            const u32x2_t a1 = lds_read_tr16(va + 8 * C::RBV);
+                            oacc[nb] = E::mfma(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb, oacc[nb]);
+                        }
+                    }
+                }
+            }
+
             wait_all_loads_here();
             __syncthreads();
         };
-        int n = 0;
-        while (n < ntiles) {
-            for (; n < ntiles && !bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) generic_step(n);
-            for (; n < ntiles && bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) full_step(n);
+        if constexpr (!SOFTMAX && !RAB && D == 128 && DV == 128) {
+            // Tiles visible to every valid row of the work-group run through the
+            // software-pipelined body, in a loop of their own; the others through the
+            // generic body.  (Choosing between the two bodies per tile inside one loop
+            // made the compiler copy the 64 output accumulators between two register
+            // sets on every tile.)
+            auto full_step = [&](int n) {
+                if (n == ntiles - 1) reserve_next();
+                const int buf = n & 1;
+                const int t_next = n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
+                silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
+                                          [&](int idx) {
+                                              if (idx < LPT) issue_one(t_next, buf ^ 1, idx);
+                                          });
+                wait_all_loads_here();
+                __syncthreads();
+            };
+            int n = 0;
+            while (n < ntiles) {
+                for (; n < ntiles && !bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) generic_step(n);
+                for (; n < ntiles && bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) full_step(n);
+            }
+        } else {
+            for (int n = 0; n < ntiles; ++n) generic_step(n);
         }
-    } else {
-        for (int n = 0; n < ntiles; ++n) generic_step(n);
-    }
 
-    // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
-    float scale = RAB ? s.attn_scale : s.attn_scale * p.alpha;
-    float lse_val = 0.f;
-    if constexpr (SOFTMAX) {
-        const float l = l_run + __shfl_xor(l_run, 32);
-        scale = l > 0.f ? s.attn_scale / l : 0.f;
-        lse_val = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
-    }
-    if (!span.valid) return;
-    const int64_t grow = s.q0 + bp.row;  // token row of o
-    if constexpr (!SPLIT) {
-        uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * DV + 4 * g;
-#pragma unroll
-        for (int nb = 0; nb < C::NDB; ++nb) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x16_t &a = oacc[nb];
-                *(u32x2_t *)(op + nb * 32 + 8 * i4) =
-                    u32x2_t{E::pack2(a[4 * i4] * scale, a[4 * i4 + 1] * scale),
-                            E::pack2(a[4 * i4 + 2] * scale, a[4 * i4 + 3] * scale)};
-            }
-        }
+        // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
+        float scale = RAB ? s.attn_scale : s.attn_scale * p.alpha;
+        float lse_val = 0.f;
         if constexpr (SOFTMAX) {
-            if (p.lse != nullptr && g == 0) {
-                const int64_t li = p.jagged ? (int64_t)h * p.total_rows + grow
-                                            : ((int64_t)bp.it.b * p.H + h) * p.seqlen_q + bp.row;
-                p.lse[li] = lse_val;
+            const float l = l_run + __shfl_xor(l_run, 32);
+            scale = l > 0.f ? s.attn_scale / l : 0.f;
+            lse_val = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+        }
+        if (!span.valid) return;
+        const int64_t grow = s.q0 + bp.row;  // token row of o
+        if constexpr (!SPLIT) {
+            uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * DV + 4 * g;
+    #pragma unroll
+            for (int nb = 0; nb < C::NDB; ++nb) {
+    #pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x16_t &a = oacc[nb];
+                    *(u32x2_t *)(op + nb * 32 + 8 * i4) =
+                        u32x2_t{E::pack2(a[4 * i4] * scale, a[4 * i4 + 1] * scale),
+                                E::pack2(a[4 * i4 + 2] * scale, a[4 * i4 + 3] * scale)};
+                }
+            }
+            if constexpr (SOFTMAX) {
+                if (p.lse != nullptr && g == 0) {
+                    const int64_t li = p.jagged ? (int64_t)h * p.total_rows + grow
+                                                : ((int64_t)bp.it.b * p.H + h) * p.seqlen_q + bp.row;
+                    p.lse[li] = lse_val;
+                }
+            }
+        } else {
+            // fp32 partials, already multiplied by attn_scale (softmax: normalised
+            // by this split's own sum; the combine pass reweights by the LSEs)
+            const int64_t prow = ((int64_t)bp.it.sp * p.total_rows + grow) * p.H + h;
+            float *pp = p.part_o + prow * DV + 4 * g;
+    #pragma unroll
+            for (int nb = 0; nb < C::NDB; ++nb) {
+    #pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x16_t &a = oacc[nb];
+                    *(f32x4_t *)(pp + nb * 32 + 8 * i4) =
+                        f32x4_t{a[4 * i4] * scale, a[4 * i4 + 1] * scale, a[4 * i4 + 2] * scale,
+                                a[4 * i4 + 3] * scale};
+                }
+            }
+            if constexpr (SOFTMAX) {
+                if (g == 0) p.part_lse[prow] = lse_val;
             }
         }
-    } else {
-        // fp32 partials, already multiplied by attn_scale (softmax: normalised
-        // by this split's own sum; the combine pass reweights by the LSEs)
-        const int64_t prow = ((int64_t)bp.it.sp * p.total_rows + grow) * p.H + h;
-        float *pp = p.part_o + prow * DV + 4 * g;
-#pragma unroll
-        for (int nb = 0; nb < C::NDB; ++nb) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x16_t &a = oacc[nb];
-                *(f32x4_t *)(pp + nb * 32 + 8 * i4) =
-                    f32x4_t{a[4 * i4] * scale, a[4 * i4 + 1] * scale, a[4 * i4 + 2] * scale,
-                            a[4 * i4 + 3] * scale};
+    };
+
+    // Persistent schedule: the grid holds about as many work-groups as fit on the
+    // chip at once, and each takes items until none are left.  Items 8 i + x of
+    // the schedule-2 order form XCD x's queue (its own (b, h) pairs, whose keys
+    // its L2 holds).  take() turns the reservation (made now if the item had no
+    // tiles) into an item or, once the own queue is empty, tries the other
+    // queues in turn; counters only grow, so every work-group ends after at most
+    // all items plus 8 failed takes.  The result reaches all waves through LDS.
+    // (The item count fits in int32: the launch checks it.)
+    const uint32_t per_queue = (uint32_t)(p.bh_pad / 8) * (uint32_t)p.num_qt * (uint32_t)p.num_splits;
+    auto take = [&](int k) -> int32_t {
+        if (threadIdx.x == 0) {
+            if (reserved == kNone) reserved = atomicAdd(&p.queue[xq], 1u);
+            int32_t r = reserved < per_queue ? 8 * (int32_t)reserved + xq : -1;
+            reserved = kNone;
+            for (int t = 1; t < 8 && r < 0; ++t) {
+                const int y = (xq + t) & 7;
+                const uint32_t i = atomicAdd(&p.queue[y], 1u);
+                if (i < per_queue) r = 8 * (int32_t)i + y;
             }
+            next_item[k & 1] = r;
         }
-        if constexpr (SOFTMAX) {
-            if (g == 0) p.part_lse[prow] = lse_val;
-        }
-    }
+        // two slots: a wave still reading slot k & 1 cannot see it overwritten
+        // before it has passed the barrier of take k + 1
+        __syncthreads();
+        // work-group uniform: keeps the loop and everything derived from the
+        // item in scalar registers
+        return __builtin_amdgcn_readfirstlane(next_item[k & 1]);
+    };
+    // The kernel arguments are re-read for every item through a pointer the
+    // compiler cannot see through; otherwise it hoists their loads out of the
+    // item loop and keeps the values live across it, in registers the tile loop
+    // needs.
+    auto args = [&]() -> const KernelParams & {
+        auto *a = (const __attribute__((address_space(4))) KernelParams *)
+            __builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(a));
+        return *(const KernelParams *)a;
+    };
+    // without a queue: one item per work-group, the work-group id
+    const bool persistent = p.queue != nullptr;
+    int k = 0;
+    for (int32_t w = persistent ? take(k++) : (int32_t)blockIdx.x; w >= 0; w = persistent ? take(k++) : -1)
+        run_item(args(), w);
 }
 
 // Split-KV combine: one thread per (row, head, 4 columns); the 32 threads of a
@@ -978,7 +1046,7 @@ template <int BN, int NW>
 __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
     __shared__ int32_t red[4 * NW];
     BlockPlan bp;
-    if (!plan_block<BN, NW>(p, false, bp, red)) return;
+    if (!plan_block<BN, NW>(p, false, bp, red, blockIdx.x)) return;
     const int lane = threadIdx.x & 63, g = lane >> 5;
     unsigned long long mine = 0;
     const int ntiles = bp.tiles.count();
@@ -1001,20 +1069,63 @@ __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, uns
 }
 
 __global__ void hstu_zero_u64(unsigned long long *x) { *x = 0; }
+// zero fill by a kernel rather than a memset node, so that the launch sequence
+// can be captured into a graph and replayed
+__global__ void hstu_zero_u32(uint32_t *x, int n) {
+    if ((int)threadIdx.x < n) x[threadIdx.x] = 0;
+}
 
 // ------------------------------------------------------------------ launchers
 
+// compute units of the current device (cached per device)
+static int current_device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Work-groups of kernel K resident per CU (cached per kernel; the kernels'
+// resources do not depend on the device among gfx950 parts).
+template <void (*K)(KernelParams)>
+static int resident_per_cu(int threads) {
+    static std::atomic<int> cache{0};
+    int n = cache.load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, K, threads, 0) != hipSuccess || n < 1) n = 1;
+        cache.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+template <void (*K)(KernelParams)>
+static hipError_t launch_items(const KernelParams &p, int threads, hipStream_t stream) {
+    const int64_t items = grid_size(p);
+    if (items <= 0) return hipSuccess;
+    int64_t grid = items;
+    if (p.queue != nullptr) {
+        // persistent: as many work-groups as are resident at once (a multiple of
+        // the 8 XCDs), never more than there are items
+        const int64_t slots = (int64_t)current_device_cus() * resident_per_cu<K>(threads);
+        grid = slots >= 8 ? (slots / 8) * 8 : 8;
+        if (grid > items) grid = items;
+        hipLaunchKernelGGL(hstu_zero_u32, dim3(1), dim3(64), 0, stream, p.queue, kQueueWords);
+    }
+    hipLaunchKernelGGL(K, dim3((unsigned)grid), dim3(threads), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int DT, int D, int DV, bool SOFTMAX, bool SPLIT>
 static hipError_t launch_one(const KernelParams &p, hipStream_t stream) {
-    const int64_t grid = grid_size(p);
-    if (grid <= 0) return hipSuccess;
+    constexpr int threads = 64 * waves_for(D);
     if (p.rab_pos != nullptr || p.rab_ts != nullptr)
-        hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, true>), dim3((unsigned)grid),
-                           dim3(64 * waves_for(D)), 0, stream, p);
-    else
-        hipLaunchKernelGGL((hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, false>), dim3((unsigned)grid),
-                           dim3(64 * waves_for(D)), 0, stream, p);
-    return hipGetLastError();
+        return launch_items<hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, true>>(p, threads, stream);
+    return launch_items<hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, false>>(p, threads, stream);
 }
 
 template <int DT, int D, int DV>

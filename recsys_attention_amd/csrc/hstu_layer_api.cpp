@@ -8,6 +8,7 @@
 #include "hstu_api_internal.h"
 #include "hstu_layer.h"
 #include "hstu_layer_launch.h"
+#include "hstu_params.h"
 
 using hstu::api::fail;
 
@@ -144,8 +145,9 @@ hstu_status_t check_layer(const hstu_layer_args_t *a, LayerDims &d) {
     return HSTU_OK;
 }
 
+// projection [n][n1], attention output [n][H dv], the attention's work counters
 size_t layer_ws(const LayerDims &d) {
-    return align256((size_t)d.n * d.n1 * 2) + align256((size_t)d.n * d.hv * 2);
+    return align256((size_t)d.n * d.n1 * 2) + align256((size_t)d.n * d.hv * 2) + hstu::kQueueBytes;
 }
 
 }  // namespace
@@ -213,7 +215,8 @@ hstu_status_t hstu_layer_fwd(const hstu_layer_args_t *args, void *ws, size_t ws_
     at.o = ao;
     at.o_tok_stride = d.hv;
     at.lse = nullptr;
-    if ((st = hstu_fwd(&at, nullptr, 0, hip_stream)) != HSTU_OK) return st;
+    void *aq = (char *)ao + align256((size_t)d.n * d.hv * 2);
+    if ((st = hstu_fwd(&at, aq, hstu::kQueueBytes, hip_stream)) != HSTU_OK) return st;
 
     // (c) Z = Norm(A) * U in place, then out = X + Z W2^T + b2
     hstu_norm_gate_args_t ng = {};

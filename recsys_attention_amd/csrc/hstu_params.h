@@ -38,6 +38,13 @@ struct KernelParams {
     const float *rab_time;   // [H][HSTU_RAB_TIME_BUCKETS]
     const float *rab_pos;    // [H][rab_pos_len]
     int32_t rab_pos_len;
+    // persistent schedule: kQueueWords work counters, zeroed before the launch
+    // (nullptr: one work item per work-group, the work-group id)
+    uint32_t *queue;
 };
+
+// work counters of the persistent schedule: one per XCD queue
+constexpr int kQueueWords = 8;
+constexpr size_t kQueueBytes = 256;  // workspace reserved for them
 
 }  // namespace hstu

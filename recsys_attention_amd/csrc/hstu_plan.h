@@ -184,11 +184,13 @@ struct WorkItem {
 // turn, so id % 8 is the XCD; both orders keep every (b, h) on one XCD):
 //  1: q-tile levels, heaviest (last) q-tile of every (b, h) first;
 //  2: per XCD, the (b, h) pairs one after another, each with all its q-tiles
-//     heaviest first, so the q-tiles reading the same keys run together.
+//     heaviest first, so the q-tiles reading the same keys run together;
+//  3: the order of 2, taken from per-XCD queues by a persistent grid (the
+//     item index replaces the work-group id).
 HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
     WorkItem it;
     int64_t bh, rest;
-    if (p.schedule == 2) {
+    if (p.schedule >= 2) {
         const int64_t xcd = w % 8, loc = w / 8;
         const int64_t per_bh = (int64_t)p.num_qt * p.num_splits;
         bh = (loc / per_bh) * 8 + xcd;

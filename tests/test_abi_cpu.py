@@ -87,7 +87,7 @@ def test_valid_args_pass(lib):
     (dict(alpha=float("nan")), _abi.HSTU_ERR_INVALID_ARG),
     (dict(lse=0x70000), _abi.HSTU_ERR_INVALID_ARG),         # lse without softmax
     (dict(causal=2), _abi.HSTU_ERR_INVALID_ARG),
-    (dict(schedule=3), _abi.HSTU_ERR_INVALID_ARG),
+    (dict(schedule=4), _abi.HSTU_ERR_INVALID_ARG),
     (dict(jagged=0, seqlen_kv=5), _abi.HSTU_ERR_INVALID_ARG),  # batched self needs equal lengths
     # relative attention bias
     (dict(cross=1, seq_offsets_kv=0x58000, rab_pos=0xa0000, rab_pos_len=8), _abi.HSTU_ERR_UNSUPPORTED),
@@ -112,18 +112,31 @@ def test_null_args(lib):
 
 def test_workspace_size_and_checks(lib):
     a = _args(softmax=1)
-    assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 1) == 0
+    # schedule left to the library: room for the persistent schedule's counters
+    assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 1) == 256
     n = lib.hstu_fwd_workspace_size(ctypes.byref(a), 16)
     rows = 8038 * 4 * 16
     o_bytes = (rows * 128 * 4 + 255) // 256 * 256
-    assert n == o_bytes + rows * 4
+    lse_bytes = (rows * 4 + 255) // 256 * 256
+    assert n == o_bytes + lse_bytes + 256
+    # a schedule without counters needs no workspace of its own
+    a2 = _args(softmax=1, schedule=2)
+    assert lib.hstu_fwd_workspace_size(ctypes.byref(a2), 1) == 0
+    assert lib.hstu_fwd_workspace_size(ctypes.byref(a2), 16) == o_bytes + lse_bytes
     assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 0) == 0
     assert lib.hstu_fwd_workspace_size(ctypes.byref(a), _abi.HSTU_MAX_SPLITS + 1) == 0
     # missing or short workspace is reported before any launch
     assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, None, 0, None) == _abi.HSTU_ERR_WORKSPACE
-    assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, ctypes.c_void_p(0x90000), n - 1,
+    assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, ctypes.c_void_p(0x90000), n - 257,
                                 None) == _abi.HSTU_ERR_WORKSPACE
     assert lib.hstu_fwd_splitkv(ctypes.byref(a), 0, None, 0, None) == _abi.HSTU_ERR_INVALID_ARG
+    # the persistent schedule asked for explicitly needs its counters
+    a3 = _args(softmax=1, schedule=3)
+    assert lib.hstu_fwd(ctypes.byref(a3), None, 0, None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_fwd(ctypes.byref(a3), ctypes.c_void_p(0x90000), 255, None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_fwd(ctypes.byref(a3), ctypes.c_void_p(0x90008), 256, None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_fwd_splitkv(ctypes.byref(a3), 16, ctypes.c_void_p(0x90000), n - 1,
+                                None) == _abi.HSTU_ERR_WORKSPACE
 
 
 def test_status_strings(lib):
@@ -227,11 +240,12 @@ def test_layer_workspace_size(lib):
     n, H, d = 8038, 4, 128
     proj = (n * 2 * H * (d + d) * 2 + 255) // 256 * 256
     att = (n * H * d * 2 + 255) // 256 * 256
-    assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == proj + att
+    queue = 256  # the attention's work counters
+    assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == proj + att + queue
     assert lib.hstu_layer_fwd(ctypes.byref(a), None, 0, None) == _abi.HSTU_ERR_WORKSPACE
-    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), proj + att - 1,
+    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), proj + att + queue - 1,
                               None) == _abi.HSTU_ERR_WORKSPACE
-    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700010), proj + att,
+    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700010), proj + att + queue,
                               None) == _abi.HSTU_ERR_WORKSPACE  # not 256-byte aligned
 
 

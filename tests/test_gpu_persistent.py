@@ -1,0 +1,87 @@
+"""The persistent schedule (3: a resident grid taking work items from per-XCD
+queues) against the one-work-group-per-item schedule (2).  Both run the same
+per-item code on the same item order, so their outputs must agree bit for bit;
+the other GPU tests compare the default schedule (3 when the workspace is
+given, which the binding does) with the oracle."""
+import pytest
+import torch
+
+import workloads as W
+from hip_runner import DeviceInputs
+from test_gpu_sweep import _case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import recsys_attention_amd as hip
+    hip._abi.load()  # raises when the library is missing: no silent fallback
+
+
+def _both(dev, **kw):
+    a = dev.forward(schedule=2, **kw)
+    b = dev.forward(schedule=3, **kw)
+    torch.cuda.synchronize()
+    return (a if isinstance(a, tuple) else (a,)), (b if isinstance(b, tuple) else (b,))
+
+
+def _same(a, b, what):
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.float32 else x.view(torch.int32),
+                           y.view(torch.uint8) if y.dtype != torch.float32 else y.view(torch.int32)), what
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_persistent_matches_per_item_grid_random(seed):
+    w, splits, rab = _case(seed)
+    print(f"case {w.name}: d={w.hdim_qk}/{w.hdim_v} softmax={w.softmax} jagged={w.jagged} "
+          f"cross={w.cross} splits={splits} bias={rab is not None}", flush=True)
+    a, b = _both(DeviceInputs(w), num_splits=splits, rab=rab)
+    _same(a, b, w.name)
+
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_persistent_matches_per_item_grid_named(name):
+    w = W.config(name)
+    print(f"case {name}", flush=True)
+    a, b = _both(DeviceInputs(w), num_splits=w.num_splits)
+    _same(a, b, name)
+
+
+def test_persistent_with_bias_long_causal():
+    w = W.config("jagged_silu_bf16_d128_causal_long")
+    rab = W.rab_inputs(w, 11, pos_len=2048)
+    print("case jagged_silu_bf16_d128_causal_long + bias", flush=True)
+    a, b = _both(DeviceInputs(w), rab=rab)
+    _same(a, b, "long causal + bias")
+
+
+def test_workspace_reused_across_calls():
+    # the library clears the work counters before every launch: a workspace left
+    # with the counts of a finished call serves the next one
+    import recsys_attention_amd as hip
+    w1, w2 = W.config("jagged_silu_bf16_d128_local"), W.config("group4_silu_bf16_d256")
+    d1, d2 = DeviceInputs(w1), DeviceInputs(w2)
+    ws = torch.full((hip.workspace_size(d1.q, d1.k, d1.v, 1, **d1.kw),), 0x5a, dtype=torch.uint8,
+                    device="cuda")
+    print("case reuse", flush=True)
+    outs = []
+    for dev in (d1, d2, d1):
+        outs.append(hip.hstu_fwd(dev.q, dev.k, dev.v, schedule=3, workspace=ws, **dev.kw))
+    torch.cuda.synchronize()
+    _same((outs[0],), (d1.forward(schedule=2),), "first call")
+    _same((outs[1],), (d2.forward(schedule=2),), "second call")
+    _same((outs[2],), (outs[0],), "third call")
+
+
+def test_empty_and_tiny_grids():
+    # fewer items than resident work-groups, and sequences without q-tiles
+    w = W.build("tiny", dtype="bf16", batch=3, nhead=1, hdim_qk=128, hdim_v=128, jagged=True,
+                cross=False, causal=True, softmax=False, alpha=0.0,
+                groups=[W.MaskGroup(0, 0, 0, 0.0)], uih_q=[0, 5, 0], targets=[0, 1, 0], seed=3)
+    print("case tiny", flush=True)
+    a, b = _both(DeviceInputs(w))
+    _same(a, b, "tiny")
