@@ -581,7 +581,19 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     // One work item (sequence, head, q-tile, split) from plan to output.
     auto run_item = [&](const KernelParams &p, int64_t w) __attribute__((always_inline)) {
         BlockPlan bp;
-        if (!plan_block<BN, NW>(p, SPLIT, bp, red, w)) return;
+        if (!plan_block<BN, NW>(p, SPLIT, bp, red, w)) {
+            // An item past its sequence's last q-tile (or of a padding pair): the
+            // q-tiles of a pair come heaviest first, so all items before the
+            // pair's first existing q-tile are of this kind.  Move the queue past
+            // them, so that they do not each cost a take.
+            if (p.queue != nullptr && threadIdx.x == 0) {
+                const int32_t per_bh = p.num_qt * p.num_splits;
+                const int32_t i = (int32_t)(w / 8), i0 = i - i % per_bh;
+                const int32_t nq = bp.it.valid ? imin((bp.s.S_q + C::BM - 1) / C::BM, p.num_qt) : 0;
+                atomicMax(&p.queue[w % 8], (uint32_t)(i0 + (p.num_qt - nq) * p.num_splits));
+            }
+            return;
+        }
         const SeqGeom &s = bp.s;
         const RowSpan &span = bp.span;
         // the lane's constants are derived per item (an opaque copy of the thread
