@@ -178,8 +178,14 @@ size_t partial_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     return ((o_bytes + 255) / 256) * 256 + ((lse_bytes + 255) / 256) * 256;
 }
 bool wants_queue(const hstu_fwd_args_t *a) { return a->schedule == 0 || a->schedule == 3; }
+// the persistent schedule's work queues (validated arguments)
+size_t queue_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+    hstu::KernelParams p;
+    fill_params(a, num_splits, p);
+    return hstu::queue_bytes(p);
+}
 size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
-    return partial_bytes(a, num_splits) + (wants_queue(a) ? hstu::kQueueBytes : 0);
+    return partial_bytes(a, num_splits) + (wants_queue(a) ? queue_bytes(a, num_splits) : 0);
 }
 
 // Schedule and work counters of one call: the persistent schedule (3) when it
@@ -187,11 +193,11 @@ size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
 // workspace holds the counters; else schedule 2 (0) or the one asked for.
 hstu_status_t pick_schedule(const hstu_fwd_args_t *a, int32_t num_splits, void *ws, size_t ws_bytes,
                             hstu::KernelParams &p) {
-    const size_t part = partial_bytes(a, num_splits);
-    const bool room = ws != nullptr && ws_bytes >= part + hstu::kQueueBytes && aligned16(ws);
+    const size_t part = partial_bytes(a, num_splits), need = part + hstu::queue_bytes(p);
+    const bool room = ws != nullptr && ws_bytes >= need && aligned16(ws);
     if (a->schedule == 3 && !room)
         return fail(HSTU_ERR_WORKSPACE, "schedule 3 needs a 16-byte aligned workspace of %zu bytes, %zu given",
-                    part + hstu::kQueueBytes, ws ? ws_bytes : (size_t)0);
+                    need, ws ? ws_bytes : (size_t)0);
     if (wants_queue(a) && room) {
         p.schedule = 3;
         p.queue = (uint32_t *)((char *)ws + part);

@@ -33,6 +33,9 @@
 namespace hstu {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// an object in global memory (address space 1): accesses through it are global
+// loads and stores
+template <class T> using gmem_t = __attribute__((address_space(1))) T;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -128,9 +131,9 @@ struct BlockPlan {
 
 template <int BN, int NW>
 __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, BlockPlan &bp,
-                                           int32_t *red, int64_t w) {
+                                           int32_t *red, const WorkItem &item) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    bp.it = decode_work(p, w);
+    bp.it = item;
     if (!bp.it.valid) return false;
     bp.s = seq_geom(p, bp.it.b);
     const int32_t r0 = bp.it.qt * (32 * NW);
@@ -234,6 +237,7 @@ __device__ __forceinline__ i32x4_t make_rsrc_words(const void *base, uint32_t by
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_to_lds(const i32x4_t &rsrc, uint32_t lds_wave, uint32_t off) {
+    lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);  // wave-uniform by contract
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -244,6 +248,7 @@ __device__ __forceinline__ void load_to_lds(const i32x4_t &rsrc, uint32_t lds_wa
 }
 // 4 bytes per lane, landing at lds_wave + 4 i (same rules as load_to_lds).
 __device__ __forceinline__ void load_to_lds4(const i32x4_t &rsrc, uint32_t lds_wave, uint32_t off) {
+    lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);  // wave-uniform by contract
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -564,36 +569,58 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     __shared__ float pos_lds[RAB ? HSTU_RAB_MAX_POS + BN - 1 : 1];
     __shared__ __attribute__((aligned(16))) int32_t ts_lds[2][TSN];
     __shared__ u32x4_t oct_lds[RAB ? kRabBinades : 1];  // time-bucket lookup per binade
-    __shared__ int32_t next_item[2];
+    __shared__ int32_t next_item[2][2];
 
-    // Persistent schedule, work counters: the work-group's own queue is that of
-    // its XCD (work-group ids go to the 8 XCDs in turn).  Thread 0 reserves the
-    // next item from it when the current item starts its last key tile, so the
-    // atomic's latency hides behind that tile (reserving earlier would double
-    // the items in flight and with them the keys competing for the XCD's L2).
+    // The kernel arguments are re-read for every item through a pointer the
+    // compiler cannot see through; otherwise it hoists their loads out of the
+    // item loop and keeps the values live across it, in registers the tile loop
+    // needs.
+    auto args = [&]() -> const KernelParams & {
+        auto *a = (const __attribute__((address_space(4))) KernelParams *)
+            __builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(a));
+        return *(const KernelParams *)a;
+    };
+    // Persistent schedule (queues written by hstu_plan_kernel): the work-group's
+    // own queue is that of its XCD (work-group ids go to the 8 XCDs in turn).
+    // Thread 0 reserves the next item (an atomic on the queue's counter) when
+    // the current item starts its next-to-last key tile and loads the item's
+    // entry when it starts the last, so both latencies hide behind those tiles.
+    // (Reserving at the start of an item instead doubled the items in flight and
+    // with them the keys competing for the XCD's L2: 6 % slower.)  The queue's
+    // addresses are derived from the re-read arguments at each use, so that
+    // nothing of them stays live in scalar registers across the item loop.
     constexpr uint32_t kNone = 0xffffffffu;
+    constexpr uint64_t kNoItem = 0xffffffffu;  // bh = -1
     const int xq = (int)(blockIdx.x % 8);
     uint32_t reserved = kNone;
+    uint64_t entry = kNoItem;
+    bool have_entry = false;
+    // (the planning kernel fills each queue's unused tail with "no item", so
+    // one load tells both whether and which)
+    auto queue_item = [&](const KernelParams &a, int y, uint32_t i) -> uint64_t {
+        const gmem_t<uint64_t> *list = (const gmem_t<uint64_t> *)((const uint8_t *)a.queue + kQueueHeader);
+        const uint32_t per_queue = (uint32_t)(grid_size(a) / 8);
+        return i < per_queue ? list[(size_t)y * per_queue + i] : kNoItem;
+    };
     auto reserve_next = [&]() {
-        if (p.queue != nullptr && threadIdx.x == 0) reserved = atomicAdd(&p.queue[xq], 1u);
+        const KernelParams &a = args();
+        if (a.queue != nullptr && threadIdx.x == 0 && reserved == kNone)
+            reserved = atomicAdd(&a.queue[xq], 1u);
+    };
+    auto fetch_next = [&]() {
+        const KernelParams &a = args();
+        if (a.queue != nullptr && threadIdx.x == 0 && !have_entry) {
+            if (reserved == kNone) reserved = atomicAdd(&a.queue[xq], 1u);
+            entry = queue_item(a, xq, reserved);
+            have_entry = true;
+        }
     };
 
     // One work item (sequence, head, q-tile, split) from plan to output.
-    auto run_item = [&](const KernelParams &p, int64_t w) __attribute__((always_inline)) {
+    auto run_item = [&](const KernelParams &p, const WorkItem &item) __attribute__((always_inline)) {
         BlockPlan bp;
-        if (!plan_block<BN, NW>(p, SPLIT, bp, red, w)) {
-            // An item past its sequence's last q-tile (or of a padding pair): the
-            // q-tiles of a pair come heaviest first, so all items before the
-            // pair's first existing q-tile are of this kind.  Move the queue past
-            // them, so that they do not each cost a take.
-            if (p.queue != nullptr && threadIdx.x == 0) {
-                const int32_t per_bh = p.num_qt * p.num_splits;
-                const int32_t i = (int32_t)(w / 8), i0 = i - i % per_bh;
-                const int32_t nq = bp.it.valid ? imin((bp.s.S_q + C::BM - 1) / C::BM, p.num_qt) : 0;
-                atomicMax(&p.queue[w % 8], (uint32_t)(i0 + (p.num_qt - nq) * p.num_splits));
-            }
-            return;
-        }
+        if (!plan_block<BN, NW>(p, SPLIT, bp, red, item)) return;
         const SeqGeom &s = bp.s;
         const RowSpan &span = bp.span;
         // the lane's constants are derived per item (an opaque copy of the thread
@@ -737,7 +764,8 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
         // one key tile through the generic body (any mask, any variant)
         auto generic_step = [&](int n) {
-            if (n == ntiles - 1) reserve_next();
+            if (n == ntiles - 2) reserve_next();
+            if (n == ntiles - 1) fetch_next();
             const int buf = n & 1;
             const bool has_next = n + 1 < ntiles;
             // after the last tile the loads fall past the sequence's buffer range: they
@@ -853,7 +881,8 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             // made the compiler copy the 64 output accumulators between two register
             // sets on every tile.)
             auto full_step = [&](int n) {
-                if (n == ntiles - 1) reserve_next();
+                if (n == ntiles - 2) reserve_next();
+                if (n == ntiles - 1) fetch_next();
                 const int buf = n & 1;
                 const int t_next = n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
                 silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
@@ -923,48 +952,52 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     };
 
     // Persistent schedule: the grid holds about as many work-groups as fit on the
-    // chip at once, and each takes items until none are left.  Items 8 i + x of
-    // the schedule-2 order form XCD x's queue (its own (b, h) pairs, whose keys
-    // its L2 holds).  take() turns the reservation (made now if the item had no
-    // tiles) into an item or, once the own queue is empty, tries the other
-    // queues in turn; counters only grow, so every work-group ends after at most
-    // all items plus 8 failed takes.  The result reaches all waves through LDS.
-    // (The item count fits in int32: the launch checks it.)
-    const uint32_t per_queue = (uint32_t)(p.bh_pad / 8) * (uint32_t)p.num_qt * (uint32_t)p.num_splits;
-    auto take = [&](int k) -> int32_t {
+    // chip at once, and each takes items until none are left.  take() turns the
+    // prefetched entry (fetched now if the item had no tiles) into the next item
+    // or, once the own queue is empty, tries the other XCDs' queues in turn;
+    // counters only grow, so every work-group ends after at most all items plus
+    // 8 failed takes.  The entry reaches all waves through LDS.
+    auto take = [&](int k) -> int2 {
         if (threadIdx.x == 0) {
-            if (reserved == kNone) reserved = atomicAdd(&p.queue[xq], 1u);
-            int32_t r = reserved < per_queue ? 8 * (int32_t)reserved + xq : -1;
-            reserved = kNone;
-            for (int t = 1; t < 8 && r < 0; ++t) {
+            fetch_next();
+            const KernelParams &a = args();
+            uint64_t e = entry;
+            for (int t = 1; t < 8 && e == kNoItem; ++t) {
                 const int y = (xq + t) & 7;
-                const uint32_t i = atomicAdd(&p.queue[y], 1u);
-                if (i < per_queue) r = 8 * (int32_t)i + y;
+                e = queue_item(a, y, atomicAdd(&a.queue[y], 1u));
             }
-            next_item[k & 1] = r;
+            reserved = kNone;
+            have_entry = false;
+            next_item[k & 1][0] = (int32_t)(uint32_t)e;
+            next_item[k & 1][1] = (int32_t)(e >> 32);
         }
         // two slots: a wave still reading slot k & 1 cannot see it overwritten
         // before it has passed the barrier of take k + 1
         __syncthreads();
         // work-group uniform: keeps the loop and everything derived from the
         // item in scalar registers
-        return __builtin_amdgcn_readfirstlane(next_item[k & 1]);
+        return int2{__builtin_amdgcn_readfirstlane(next_item[k & 1][0]),
+                    __builtin_amdgcn_readfirstlane(next_item[k & 1][1])};
     };
-    // The kernel arguments are re-read for every item through a pointer the
-    // compiler cannot see through; otherwise it hoists their loads out of the
-    // item loop and keeps the values live across it, in registers the tile loop
-    // needs.
-    auto args = [&]() -> const KernelParams & {
-        auto *a = (const __attribute__((address_space(4))) KernelParams *)
-            __builtin_amdgcn_kernarg_segment_ptr();
-        asm volatile("" : "+s"(a));
-        return *(const KernelParams *)a;
-    };
-    // without a queue: one item per work-group, the work-group id
-    const bool persistent = p.queue != nullptr;
-    int k = 0;
-    for (int32_t w = persistent ? take(k++) : (int32_t)blockIdx.x; w >= 0; w = persistent ? take(k++) : -1)
-        run_item(args(), w);
+    // (one call site, so the item body is inlined once)
+    for (int k = 0;; ++k) {
+        WorkItem it;
+        const KernelParams &a = args();
+        if (a.queue == nullptr) {
+            // one item per work-group, the work-group id
+            if (k > 0) break;
+            it = decode_work(a, blockIdx.x);
+        } else {
+            const int2 e = take(k);
+            if (e.x < 0) break;
+            it.b = e.x / a.H;
+            it.h = e.x % a.H;
+            it.qt = e.y >> 8;
+            it.sp = e.y & 255;
+            it.valid = true;
+        }
+        run_item(args(), it);
+    }
 }
 
 // Split-KV combine: one thread per (row, head, 4 columns); the 32 threads of a
@@ -1058,7 +1091,7 @@ template <int BN, int NW>
 __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
     __shared__ int32_t red[4 * NW];
     BlockPlan bp;
-    if (!plan_block<BN, NW>(p, false, bp, red, blockIdx.x)) return;
+    if (!plan_block<BN, NW>(p, false, bp, red, decode_work(p, blockIdx.x))) return;
     const int lane = threadIdx.x & 63, g = lane >> 5;
     unsigned long long mine = 0;
     const int ntiles = bp.tiles.count();
@@ -1081,10 +1114,105 @@ __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, uns
 }
 
 __global__ void hstu_zero_u64(unsigned long long *x) { *x = 0; }
-// zero fill by a kernel rather than a memset node, so that the launch sequence
-// can be captured into a graph and replayed
-__global__ void hstu_zero_u32(uint32_t *x, int n) {
-    if ((int)threadIdx.x < n) x[threadIdx.x] = 0;
+
+// Planning kernel of the persistent schedule: work-group x writes XCD x's queue.
+// The queue holds the existing q-tiles of the XCD's (b, h) pairs (bh = x + 8k),
+// the pairs ordered from the most expensive sequence to the cheapest (cost:
+// q-tiles x keys; ties by k; at most kPlanSortPairs pairs are sorted, beyond
+// that they keep their order), each pair's q-tiles heaviest first and, per
+// q-tile, its splits.  Running the longest pairs first keeps their long q-tiles
+// out of the kernel's tail; listing only existing q-tiles spares the item loop
+// the empty ones.  It also clears the take counter.  (A kernel, not a memset,
+// so that the launch sequence can be captured into a graph and replayed.)
+constexpr int kPlanThreads = 256;
+constexpr int kPlanSortPairs = 2048;
+template <int BM>
+__global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(KernelParams p) {
+    __shared__ float key[kPlanSortPairs];
+    __shared__ int32_t order[kPlanSortPairs];
+    __shared__ int32_t scan[kPlanThreads];
+    const int x = blockIdx.x, t = threadIdx.x;
+    const int K = p.bh_pad / 8;
+    const uint32_t per_queue = (uint32_t)(grid_size(p) / 8);
+    gmem_t<uint64_t> *list = (gmem_t<uint64_t> *)((uint8_t *)p.queue + kQueueHeader) + (size_t)x * per_queue;
+    // q-tiles and cost of pair k of this queue
+    auto pair = [&](int k, int &bh, int &nq, float &cost) {
+        bh = x + 8 * k;
+        nq = 0;
+        cost = -0.5f;
+        if (bh >= p.B * p.H) return;
+        const int b = bh / p.H;
+        int S_q = p.seqlen_q, S_kv = p.seqlen_kv;
+        if (p.jagged) {
+            S_q = p.off_q[b + 1] - p.off_q[b];
+            S_kv = p.cross ? p.off_kv[b + 1] - p.off_kv[b] : S_q;
+        }
+        nq = imin((S_q + BM - 1) / BM, p.num_qt);
+        cost = (float)nq * (float)S_kv;
+    };
+    const bool sorted = K <= kPlanSortPairs;
+    if (sorted) {
+        int n = 1;
+        while (n < K) n <<= 1;
+        for (int i = t; i < n; i += kPlanThreads) {
+            int bh, nq;
+            float c = -1.0f;  // padding entries sort last
+            if (i < K) pair(i, bh, nq, c);
+            key[i] = c;
+            order[i] = i;
+        }
+        __syncthreads();
+        // bitonic sort into "a before b": larger cost first, then smaller k
+        for (int size = 2; size <= n; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = t; i < n; i += kPlanThreads) {
+                    const int j = i ^ stride;
+                    if (j > i) {
+                        const bool i_first = key[i] > key[j] || (key[i] == key[j] && order[i] < order[j]);
+                        if (((i & size) == 0) != i_first) {
+                            const float kt = key[i];
+                            key[i] = key[j];
+                            key[j] = kt;
+                            const int ot = order[i];
+                            order[i] = order[j];
+                            order[j] = ot;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+    // in order, 256 pairs at a time: inclusive scan of their item counts, then
+    // each thread writes its pair's items
+    int carry = 0;
+    for (int r0 = 0; r0 < K; r0 += kPlanThreads) {
+        const int r = r0 + t;
+        int bh = 0, nq = 0;
+        float c;
+        if (r < K) pair(sorted ? order[r] : r, bh, nq, c);
+        const int items = nq * p.num_splits;
+        scan[t] = items;
+        __syncthreads();
+        for (int o = 1; o < kPlanThreads; o <<= 1) {
+            const int v = t >= o ? scan[t - o] : 0;
+            __syncthreads();
+            scan[t] += v;
+            __syncthreads();
+        }
+        const int base = carry + scan[t] - items;
+        for (int j = 0; j < items; ++j)
+            list[base + j] = (uint64_t)(uint32_t)bh |
+                             (uint64_t)(uint32_t)((nq - 1 - j / p.num_splits) << 8 | (j % p.num_splits)) << 32;
+        carry += scan[kPlanThreads - 1];
+        __syncthreads();
+    }
+    // the rest of the queue: "no item" (bh = -1)
+    for (uint32_t i = (uint32_t)carry + t; i < per_queue; i += kPlanThreads) list[i] = 0xffffffffu;
+    if (t == 0) {
+        p.queue[x] = 0;
+        p.queue[kQueueCount + x] = (uint32_t)carry;
+    }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1115,7 +1243,7 @@ static int resident_per_cu(int threads) {
     return n;
 }
 
-template <void (*K)(KernelParams)>
+template <void (*K)(KernelParams), int D>
 static hipError_t launch_items(const KernelParams &p, int threads, hipStream_t stream) {
     const int64_t items = grid_size(p);
     if (items <= 0) return hipSuccess;
@@ -1126,7 +1254,7 @@ static hipError_t launch_items(const KernelParams &p, int threads, hipStream_t s
         const int64_t slots = (int64_t)current_device_cus() * resident_per_cu<K>(threads);
         grid = slots >= 8 ? (slots / 8) * 8 : 8;
         if (grid > items) grid = items;
-        hipLaunchKernelGGL(hstu_zero_u32, dim3(1), dim3(64), 0, stream, p.queue, kQueueWords);
+        hipLaunchKernelGGL((hstu_plan_kernel<block_m_for(D)>), dim3(8), dim3(kPlanThreads), 0, stream, p);
     }
     hipLaunchKernelGGL(K, dim3((unsigned)grid), dim3(threads), 0, stream, p);
     return hipGetLastError();
@@ -1136,8 +1264,8 @@ template <int DT, int D, int DV, bool SOFTMAX, bool SPLIT>
 static hipError_t launch_one(const KernelParams &p, hipStream_t stream) {
     constexpr int threads = 64 * waves_for(D);
     if (p.rab_pos != nullptr || p.rab_ts != nullptr)
-        return launch_items<hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, true>>(p, threads, stream);
-    return launch_items<hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, false>>(p, threads, stream);
+        return launch_items<hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, true>, D>(p, threads, stream);
+    return launch_items<hstu_fwd_kernel<DT, D, SOFTMAX, SPLIT, DV, false>, D>(p, threads, stream);
 }
 
 template <int DT, int D, int DV>

@@ -106,6 +106,7 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 struct LayerDims {
     int64_t n;
     int32_t n1, hv, hq;
+    size_t aws;  // the attention's workspace
 };
 
 hstu_status_t check_layer(const hstu_layer_args_t *a, LayerDims &d) {
@@ -142,12 +143,14 @@ hstu_status_t check_layer(const hstu_layer_args_t *a, LayerDims &d) {
     hstu_status_t st = hstu::api::validate_fwd(&t);
     if (st != HSTU_OK) return st;
     d.n = hstu::api::rows_q(&a->attn);
+    d.aws = hstu_fwd_workspace_size(&t, 1);
     return HSTU_OK;
 }
 
-// projection [n][n1], attention output [n][H dv], the attention's work counters
+// projection [n][n1], attention output [n][H dv], the attention's own workspace
+// (the persistent schedule's work queues)
 size_t layer_ws(const LayerDims &d) {
-    return align256((size_t)d.n * d.n1 * 2) + align256((size_t)d.n * d.hv * 2) + hstu::kQueueBytes;
+    return align256((size_t)d.n * d.n1 * 2) + align256((size_t)d.n * d.hv * 2) + align256(d.aws);
 }
 
 }  // namespace
@@ -216,7 +219,7 @@ hstu_status_t hstu_layer_fwd(const hstu_layer_args_t *args, void *ws, size_t ws_
     at.o_tok_stride = d.hv;
     at.lse = nullptr;
     void *aq = (char *)ao + align256((size_t)d.n * d.hv * 2);
-    if ((st = hstu_fwd(&at, aq, hstu::kQueueBytes, hip_stream)) != HSTU_OK) return st;
+    if ((st = hstu_fwd(&at, aq, d.aws, hip_stream)) != HSTU_OK) return st;
 
     // (c) Z = Norm(A) * U in place, then out = X + Z W2^T + b2
     hstu_norm_gate_args_t ng = {};

@@ -38,13 +38,18 @@ struct KernelParams {
     const float *rab_time;   // [H][HSTU_RAB_TIME_BUCKETS]
     const float *rab_pos;    // [H][rab_pos_len]
     int32_t rab_pos_len;
-    // persistent schedule: kQueueWords work counters, zeroed before the launch
-    // (nullptr: one work item per work-group, the work-group id)
+    // persistent schedule: the per-XCD work queues (layout below), written by
+    // the planning kernel before the launch; nullptr: one work item per
+    // work-group, the work-group id
     uint32_t *queue;
 };
 
-// work counters of the persistent schedule: one per XCD queue
-constexpr int kQueueWords = 8;
-constexpr size_t kQueueBytes = 256;  // workspace reserved for them
+// Work queues of the persistent schedule, in the caller's workspace:
+//   words [0, 8)    take counter of XCD queue x (cleared by the planning kernel)
+//   words [8, 16)   number of items in queue x
+//   byte 256 on     queue x's items at kQueueHeader + 8 (x * per_queue + i):
+//                   bh | (qt << 8 | split) << 32 (uint64), per_queue = grid / 8
+constexpr size_t kQueueHeader = 256;
+constexpr int kQueueCount = 8;  // word offset of the item counts
 
 }  // namespace hstu

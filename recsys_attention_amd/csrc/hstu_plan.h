@@ -185,8 +185,10 @@ struct WorkItem {
 //  1: q-tile levels, heaviest (last) q-tile of every (b, h) first;
 //  2: per XCD, the (b, h) pairs one after another, each with all its q-tiles
 //     heaviest first, so the q-tiles reading the same keys run together;
-//  3: the order of 2, taken from per-XCD queues by a persistent grid (the
-//     item index replaces the work-group id).
+//  3: per XCD, the (b, h) pairs from the most expensive sequence to the
+//     cheapest, each with its existing q-tiles heaviest first, taken from
+//     per-XCD queues by a persistent grid (the planning kernel writes the
+//     queues; decode_work is not used).
 HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
     WorkItem it;
     int64_t bh, rest;
@@ -209,6 +211,12 @@ HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
 
 HSTU_HD int64_t grid_size(const KernelParams &p) {
     return (int64_t)p.bh_pad * p.num_qt * p.num_splits;
+}
+
+// Workspace bytes of the persistent schedule's queues (header + one 8-byte entry
+// per possible item).
+HSTU_HD size_t queue_bytes(const KernelParams &p) {
+    return kQueueHeader + 8 * (size_t)grid_size(p);
 }
 
 }  // namespace hstu

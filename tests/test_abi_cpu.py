@@ -112,13 +112,15 @@ def test_null_args(lib):
 
 def test_workspace_size_and_checks(lib):
     a = _args(softmax=1)
-    # schedule left to the library: room for the persistent schedule's counters
-    assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 1) == 256
+    # schedule left to the library: room for the persistent schedule's queues
+    # (a 256-byte header and 8 bytes per possible item: 40 (b, h) pairs, 7 q-tiles
+    # of 128 rows for 881 rows, times the splits)
+    assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 1) == 256 + 8 * 40 * 7
     n = lib.hstu_fwd_workspace_size(ctypes.byref(a), 16)
     rows = 8038 * 4 * 16
     o_bytes = (rows * 128 * 4 + 255) // 256 * 256
     lse_bytes = (rows * 4 + 255) // 256 * 256
-    assert n == o_bytes + lse_bytes + 256
+    assert n == o_bytes + lse_bytes + 256 + 8 * 40 * 7 * 16
     # a schedule without counters needs no workspace of its own
     a2 = _args(softmax=1, schedule=2)
     assert lib.hstu_fwd_workspace_size(ctypes.byref(a2), 1) == 0
@@ -127,14 +129,15 @@ def test_workspace_size_and_checks(lib):
     assert lib.hstu_fwd_workspace_size(ctypes.byref(a), _abi.HSTU_MAX_SPLITS + 1) == 0
     # missing or short workspace is reported before any launch
     assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, None, 0, None) == _abi.HSTU_ERR_WORKSPACE
-    assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, ctypes.c_void_p(0x90000), n - 257,
+    assert lib.hstu_fwd_splitkv(ctypes.byref(a), 16, ctypes.c_void_p(0x90000), o_bytes + lse_bytes - 1,
                                 None) == _abi.HSTU_ERR_WORKSPACE
     assert lib.hstu_fwd_splitkv(ctypes.byref(a), 0, None, 0, None) == _abi.HSTU_ERR_INVALID_ARG
     # the persistent schedule asked for explicitly needs its counters
     a3 = _args(softmax=1, schedule=3)
     assert lib.hstu_fwd(ctypes.byref(a3), None, 0, None) == _abi.HSTU_ERR_WORKSPACE
-    assert lib.hstu_fwd(ctypes.byref(a3), ctypes.c_void_p(0x90000), 255, None) == _abi.HSTU_ERR_WORKSPACE
-    assert lib.hstu_fwd(ctypes.byref(a3), ctypes.c_void_p(0x90008), 256, None) == _abi.HSTU_ERR_WORKSPACE
+    q1 = 256 + 8 * 40 * 7
+    assert lib.hstu_fwd(ctypes.byref(a3), ctypes.c_void_p(0x90000), q1 - 1, None) == _abi.HSTU_ERR_WORKSPACE
+    assert lib.hstu_fwd(ctypes.byref(a3), ctypes.c_void_p(0x90008), q1, None) == _abi.HSTU_ERR_WORKSPACE
     assert lib.hstu_fwd_splitkv(ctypes.byref(a3), 16, ctypes.c_void_p(0x90000), n - 1,
                                 None) == _abi.HSTU_ERR_WORKSPACE
 
@@ -240,7 +243,7 @@ def test_layer_workspace_size(lib):
     n, H, d = 8038, 4, 128
     proj = (n * 2 * H * (d + d) * 2 + 255) // 256 * 256
     att = (n * H * d * 2 + 255) // 256 * 256
-    queue = 256  # the attention's work counters
+    queue = (256 + 8 * 40 * 7 + 255) // 256 * 256  # the attention's work queues
     assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == proj + att + queue
     assert lib.hstu_layer_fwd(ctypes.byref(a), None, 0, None) == _abi.HSTU_ERR_WORKSPACE
     assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), proj + att + queue - 1,

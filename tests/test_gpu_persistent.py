@@ -60,13 +60,13 @@ def test_persistent_with_bias_long_causal():
 
 
 def test_workspace_reused_across_calls():
-    # the library clears the work counters before every launch: a workspace left
-    # with the counts of a finished call serves the next one
+    # the planning kernel rewrites the queues before every launch: a workspace
+    # left with another call's queues (or garbage) serves the next one
     import recsys_attention_amd as hip
     w1, w2 = W.config("jagged_silu_bf16_d128_local"), W.config("group4_silu_bf16_d256")
     d1, d2 = DeviceInputs(w1), DeviceInputs(w2)
-    ws = torch.full((hip.workspace_size(d1.q, d1.k, d1.v, 1, **d1.kw),), 0x5a, dtype=torch.uint8,
-                    device="cuda")
+    need = max(hip.workspace_size(d.q, d.k, d.v, 1, **d.kw) for d in (d1, d2))
+    ws = torch.full((need,), 0x5a, dtype=torch.uint8, device="cuda")
     print("case reuse", flush=True)
     outs = []
     for dev in (d1, d2, d1):
