@@ -112,11 +112,13 @@ typedef struct {
     float *lse; /* softmax only, device, NULL = not saved: batched [B][H][S_q], jagged [H][total_q];
                    natural log; -inf for a row that sees no key */
     int32_t schedule; /* work order: 0 = library's choice (3 when the workspace holds the
-                         work counters, else 2), 1 = q-tile levels heavy-first, 2 = per-XCD
-                         sequence groups (each (b,h) kept on one XCD's L2), one work-group per
-                         q-tile; 3 = the order of 2 taken from per-XCD queues by a persistent
-                         grid (one resident set of work-groups, no launch gaps or tail of
-                         short work-groups; needs the workspace) */
+                         work queues and there are at least 2048 possible items, else 2);
+                         1 = q-tile levels heavy-first; 2 = per-XCD sequence groups (each
+                         (b,h) kept on one XCD's L2), one work-group per q-tile; 3 = per
+                         XCD, the (b,h) pairs longest first, taken from per-XCD work
+                         queues by a persistent grid (one resident set of work-groups: no
+                         launch gaps, no empty q-tiles, the tail stolen across XCDs; needs
+                         the workspace) */
     /* Relative attention bias (HSTU explainer, "The layer, line by line" (b) and "The
      * relative attention bias"); self-attention only (HSTU_ERR_UNSUPPORTED with cross).
      * Added to the score before the mask and the non-linearity:
@@ -135,15 +137,17 @@ typedef struct {
 hstu_status_t hstu_validate_args(const hstu_fwd_args_t *args);
 
 /* Bytes of workspace for num_splits splits (num_splits == 1: hstu_fwd): the split-KV
- * partial results, plus 256 bytes of work counters when args->schedule is 0 or 3.
- * Returns 0 on invalid arguments. */
+ * partial results, plus, when args->schedule is 0 or 3, the work queues (256 bytes
+ * and 8 per possible item: batch * nhead rounded up to 8, times the q-tiles of
+ * max_seqlen_q in 128 rows, times num_splits).  Returns 0 on invalid arguments. */
 size_t hstu_fwd_workspace_size(const hstu_fwd_args_t *args, int32_t num_splits);
 
-/* The forward operator: one fused kernel per call (plus a one-work-group kernel that
- * clears the work counters, for schedule 3).  ws may be NULL: then schedule 0 runs
+/* The forward operator: one fused kernel per call (plus, for schedule 3, an 8-work-
+ * group kernel that writes the work queues).  ws may be NULL: then schedule 0 runs
  * as 2, and schedule 3 fails with HSTU_ERR_WORKSPACE.  A workspace of at least
  * hstu_fwd_workspace_size(args, 1) bytes, 16-byte aligned, is used by schedule 0
- * and 3; calls that share a workspace must not overlap in time. */
+ * and 3; its contents need no initialisation; calls that share a workspace must
+ * not overlap in time. */
 hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Split-KV forward (README "Split-KV"): the key axis of every sequence is cut into
@@ -151,8 +155,8 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
  * partial outputs (and LSEs for softmax) into ws; a second kernel combines them into
  * o (and lse).  The result equals hstu_fwd's up to fp32 reassociation.
  * 1 <= num_splits <= HSTU_MAX_SPLITS; ws_bytes >= the partial results' share of
- * hstu_fwd_workspace_size() (without the 256 bytes of counters schedule 0 runs
- * as 2; schedule 3 needs them). */
+ * hstu_fwd_workspace_size() (without room for the work queues schedule 0 runs as
+ * 2; schedule 3 needs it). */
 hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, void *ws,
                                size_t ws_bytes, void *hip_stream);
 

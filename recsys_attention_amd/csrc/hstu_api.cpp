@@ -188,9 +188,12 @@ size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     return partial_bytes(a, num_splits) + (wants_queue(a) ? queue_bytes(a, num_splits) : 0);
 }
 
-// Schedule and work counters of one call: the persistent schedule (3) when it
-// is asked for, or when the schedule is left to the library (0) and the
-// workspace holds the counters; else schedule 2 (0) or the one asked for.
+constexpr int64_t kPersistentItems = 2048;
+
+// Schedule and work queues of one call: the persistent schedule (3) when it is
+// asked for, or when the schedule is left to the library (0), the workspace
+// holds the queues and the grid is large; else schedule 2 (0) or the one asked
+// for.
 hstu_status_t pick_schedule(const hstu_fwd_args_t *a, int32_t num_splits, void *ws, size_t ws_bytes,
                             hstu::KernelParams &p) {
     const size_t part = partial_bytes(a, num_splits), need = part + hstu::queue_bytes(p);
@@ -198,7 +201,11 @@ hstu_status_t pick_schedule(const hstu_fwd_args_t *a, int32_t num_splits, void *
     if (a->schedule == 3 && !room)
         return fail(HSTU_ERR_WORKSPACE, "schedule 3 needs a 16-byte aligned workspace of %zu bytes, %zu given",
                     need, ws ? ws_bytes : (size_t)0);
-    if (wants_queue(a) && room) {
+    // left to the library, the persistent grid runs only where its planning
+    // kernel (one short launch) is small against the work: from kPersistentItems
+    // possible items, four per resident work-group on a 256-CU part
+    const bool worth = a->schedule == 3 || hstu::grid_size(p) >= kPersistentItems;
+    if (wants_queue(a) && room && worth) {
         p.schedule = 3;
         p.queue = (uint32_t *)((char *)ws + part);
     } else {

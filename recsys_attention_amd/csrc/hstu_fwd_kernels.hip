@@ -1124,20 +1124,21 @@ __global__ void hstu_zero_u64(unsigned long long *x) { *x = 0; }
 // out of the kernel's tail; listing only existing q-tiles spares the item loop
 // the empty ones.  It also clears the take counter.  (A kernel, not a memset,
 // so that the launch sequence can be captured into a graph and replayed.)
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 64;  // one wave: the barriers cost next to nothing
 constexpr int kPlanSortPairs = 2048;
 template <int BM>
 __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(KernelParams p) {
     __shared__ float key[kPlanSortPairs];
     __shared__ int32_t order[kPlanSortPairs];
+    __shared__ int32_t nq_of[kPlanSortPairs];  // q-tiles of pair k (sorted queues)
     __shared__ int32_t scan[kPlanThreads];
     const int x = blockIdx.x, t = threadIdx.x;
     const int K = p.bh_pad / 8;
     const uint32_t per_queue = (uint32_t)(grid_size(p) / 8);
     gmem_t<uint64_t> *list = (gmem_t<uint64_t> *)((uint8_t *)p.queue + kQueueHeader) + (size_t)x * per_queue;
     // q-tiles and cost of pair k of this queue
-    auto pair = [&](int k, int &bh, int &nq, float &cost) {
-        bh = x + 8 * k;
+    auto pair = [&](int k, int &nq, float &cost) {
+        const int bh = x + 8 * k;
         nq = 0;
         cost = -0.5f;
         if (bh >= p.B * p.H) return;
@@ -1155,11 +1156,12 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(KernelParams p)
         int n = 1;
         while (n < K) n <<= 1;
         for (int i = t; i < n; i += kPlanThreads) {
-            int bh, nq;
+            int nq = 0;
             float c = -1.0f;  // padding entries sort last
-            if (i < K) pair(i, bh, nq, c);
+            if (i < K) pair(i, nq, c);
             key[i] = c;
             order[i] = i;
+            nq_of[i] = nq;
         }
         __syncthreads();
         // bitonic sort into "a before b": larger cost first, then smaller k
@@ -1183,14 +1185,21 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(KernelParams p)
             }
         }
     }
-    // in order, 256 pairs at a time: inclusive scan of their item counts, then
-    // each thread writes its pair's items
+    // in order, kPlanThreads pairs at a time: inclusive scan of their item
+    // counts, then each thread writes its pair's items
     int carry = 0;
     for (int r0 = 0; r0 < K; r0 += kPlanThreads) {
         const int r = r0 + t;
-        int bh = 0, nq = 0;
-        float c;
-        if (r < K) pair(sorted ? order[r] : r, bh, nq, c);
+        int k = 0, nq = 0;
+        if (r < K) {
+            k = sorted ? order[r] : r;
+            float c;
+            if (sorted)
+                nq = nq_of[k];
+            else
+                pair(k, nq, c);
+        }
+        const int bh = x + 8 * k;
         const int items = nq * p.num_splits;
         scan[t] = items;
         __syncthreads();
@@ -1200,10 +1209,10 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(KernelParams p)
             scan[t] += v;
             __syncthreads();
         }
-        const int base = carry + scan[t] - items;
-        for (int j = 0; j < items; ++j)
-            list[base + j] = (uint64_t)(uint32_t)bh |
-                             (uint64_t)(uint32_t)((nq - 1 - j / p.num_splits) << 8 | (j % p.num_splits)) << 32;
+        int e = carry + scan[t] - items;
+        for (int qt = nq - 1; qt >= 0; --qt)
+            for (int sp = 0; sp < p.num_splits; ++sp)
+                list[e++] = (uint64_t)(uint32_t)bh | (uint64_t)(uint32_t)(qt << 8 | sp) << 32;
         carry += scan[kPlanThreads - 1];
         __syncthreads();
     }
