@@ -85,3 +85,35 @@ def test_empty_and_tiny_grids():
     print("case tiny", flush=True)
     a, b = _both(DeviceInputs(w))
     _same(a, b, "tiny")
+
+
+def test_persistent_schedule_in_a_graph():
+    # the planning kernel (not a memset node) rewrites the queues on every
+    # replay; each replay, with eager work and synchronisations in between, must
+    # reproduce the eager result bit for bit
+    import recsys_attention_amd as hip
+    w = W.config("jagged_silu_bf16_d128_causal_long")
+    dev = DeviceInputs(w)
+    eager = dev.forward(schedule=3)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    ws = torch.empty(hip.workspace_size(dev.q, dev.k, dev.v, 1, **dev.kw), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        hip.hstu_fwd(dev.q, dev.k, dev.v, schedule=3, out=out, workspace=ws, **dev.kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("case graph capture", flush=True)
+    with torch.cuda.graph(g):
+        hip.hstu_fwd(dev.q, dev.k, dev.v, schedule=3, out=out, workspace=ws, **dev.kw)
+    for r in range(4):
+        out.zero_()
+        ws.fill_(0x5a)  # garbage in the queues: the replay must rewrite them
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same((out,), (eager,), f"replay {r}")
+        dev.forward(schedule=2)  # eager work between replays
+        torch.cuda.synchronize()
