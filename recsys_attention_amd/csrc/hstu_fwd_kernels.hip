@@ -756,6 +756,12 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         // with the bias the scores already carry alpha (rab_block)
         const float neg_alpha_log2e = RAB ? -kLog2e : -p.alpha * kLog2e;
         const float sc_soft = RAB ? kLog2e : p.alpha * kLog2e;
+        // the bias's scalars, held in registers: re-read from the (re-read per
+        // item) arguments inside the tile loop, their loads each waited for the
+        // outstanding LDS reads too (a scalar-memory wait)
+        float rab_alpha = p.alpha;
+        int32_t rab_pos_len = p.rab_pos_len;
+        if constexpr (RAB) asm volatile("" : "+s"(rab_alpha), "+s"(rab_pos_len));
         const uint8_t *lds0 = &lds[0][0];
 
         if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
@@ -799,7 +805,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 // ---- mask + non-linearity; element i of block kb is key
                 //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
                 if constexpr (RAB)
-                    rab_tile<C::NKB, BN>(sacc, p.alpha, bp.row, j0, g, wrow0, pos_lds, p.rab_pos_len,
+                    rab_tile<C::NKB, BN>(sacc, rab_alpha, bp.row, j0, g, wrow0, pos_lds, rab_pos_len,
                                          ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
                                          has_time, lane);
                 if constexpr (!SOFTMAX) {
