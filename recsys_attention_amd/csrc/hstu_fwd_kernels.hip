@@ -643,7 +643,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
         // ---- Q^T operand: lane holds d = 16*kk + 8*g .. +7 of its row
         u32x4_t qreg[C::KSTEPS];
-    #pragma unroll
+#pragma unroll
         for (int kk = 0; kk < C::KSTEPS; ++kk)
             qreg[kk] = buf_load16(qr, (uint32_t)bp.row * qs2 + (kk * 16 + g * 8) * 2);
 
@@ -659,14 +659,14 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         constexpr bool kRowsK = C::NT % C::CPR == 0, kRowsV = C::NT % C::CPRV == 0;
         constexpr int RPC = kRowsK ? C::NT / C::CPR : 0, RPCV = kRowsV ? C::NT / C::CPRV : 0;
         uint32_t k_lane[C::LOADS], v_lane[C::LOADS_V];
-    #pragma unroll
+#pragma unroll
         for (int c = 0; c < C::LOADS; ++c) {
             const int phys = kRowsK ? tid : c * C::NT + tid;
             const int row = phys / C::CPR, pc = phys % C::CPR;
             const int rsw = (RPC & kKSwz) == 0 ? row : c * RPC + row;
             k_lane[c] = (uint32_t)row * ks2 + (uint32_t)(pc ^ (rsw & kKSwz)) * 16;
         }
-    #pragma unroll
+#pragma unroll
         for (int c = 0; c < C::LOADS_V; ++c) {
             const int phys = kRowsV ? tid : c * C::NT + tid;
             const int row = phys / C::CPRV, pc = phys % C::CPRV;
@@ -726,7 +726,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             }
         };
         auto issue_loads = [&](int t, int b) {
-    #pragma unroll
+#pragma unroll
             for (int idx = 0; idx < LPT; ++idx) issue_one(t, b, idx);
             issue_ts(t, b);
         };
@@ -737,20 +737,20 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         //  lane offsets and later k-steps repeat them one swizzle period further on)
         constexpr int NKA = kKSwz ? (kKSwz + 1) / 2 : 1, NVA = kVSwz == 4 ? 4 : (kVSwz == 2 ? 2 : 1);
         uint32_t k_addr[NKA];
-    #pragma unroll
+#pragma unroll
         for (int m = 0; m < NKA; ++m)
             k_addr[m] = (uint32_t)(r32 * C::RB + (((2 * m + g) ^ (r32 & kKSwz)) * 16));
         // V^T operand (transposed read): row K0 + 4g + (i/4), columns 32nb + 16hb + 4(i%4)
         const int i16 = lane & 15, hb = (lane >> 4) & 1;
         const int vy = kVSwz * ((i16 >> 2) & 3);
         uint32_t v_addr[NVA];
-    #pragma unroll
+#pragma unroll
         for (int b2 = 0; b2 < NVA; ++b2)
             v_addr[b2] = (uint32_t)(C::TILE_BYTES + (4 * g + (i16 >> 2)) * C::RBV +
                                     (((4 * b2 + 2 * hb + ((i16 & 3) >> 1)) ^ vy) * 16) + (i16 & 1) * 8);
 
         f32x16_t oacc[C::NDB];
-    #pragma unroll
+#pragma unroll
         for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] = f32x16_t{};
         float m_run = -INFINITY, l_run = 0.f;
         // with the bias the scores already carry alpha (rab_block)
@@ -791,11 +791,11 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 __builtin_amdgcn_s_setprio(1);
                 // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
                 f32x16_t sacc[C::NKB];
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16_t{};
-    #pragma unroll
+#pragma unroll
                 for (int kk = 0; kk < C::KSTEPS; ++kk) {
-    #pragma unroll
+#pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb) {
                         const uint8_t *ka = stage + k_addr[kk % NKA] + kb * 32 * C::RB + (kk / NKA) * (NKA * 32);
                         sacc[kb] = E::mfma(*(const u32x4_t *)ka, qreg[kk], sacc[kb]);
@@ -811,22 +811,22 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 if constexpr (!SOFTMAX) {
                     // p = x sigmoid(alpha x); the factor alpha of SiLU(alpha x) goes into the epilogue
                     if (wave_mask) {
-    #pragma unroll
+#pragma unroll
                         for (int kb = 0; kb < C::NKB; ++kb)
                             silu_block<true>(sacc[kb], neg_alpha_log2e, span, j0 + kb * 32 + 4 * g);
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int kb = 0; kb < C::NKB; ++kb)
                             silu_block<false>(sacc[kb], neg_alpha_log2e, span, 0);
                     }
                 } else {
                     float mx = -INFINITY;
                     if (wave_mask) {
-    #pragma unroll
+#pragma unroll
                         for (int kb = 0; kb < C::NKB; ++kb)
                             mx = fmaxf(mx, scale_block<true>(sacc[kb], sc_soft, span, j0 + kb * 32 + 4 * g));
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int kb = 0; kb < C::NKB; ++kb)
                             mx = fmaxf(mx, scale_block<false>(sacc[kb], sc_soft, span, 0));
                     }
@@ -836,14 +836,14 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                     const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
                     if (__ballot(corr != 1.0f) != 0) {
                         l_run *= corr;
-    #pragma unroll
+#pragma unroll
                         for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] *= corr;
                     }
                     m_run = m_new;
                     float lsum = 0.f;
-    #pragma unroll
+#pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb) {
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 16; ++i) {
                             const float e = __builtin_amdgcn_exp2f(sacc[kb][i] - m_use);
                             lsum += e;
@@ -856,9 +856,9 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 __builtin_amdgcn_s_setprio(0);
                 // ---- O^T += V^T P^T; MFMA step (kb, t2) covers keys
                 //      32kb + 16t2 + {4g..4g+3, 8+4g..8+4g+3} in both operands
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb) {
-    #pragma unroll
+#pragma unroll
                     for (int t2 = 0; t2 < 2; ++t2) {
                         const int i0 = 8 * t2;
                         const u32x4_t pb = {E::pack2(sacc[kb][i0 + 0], sacc[kb][i0 + 1]),
@@ -866,7 +866,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                                             E::pack2(sacc[kb][i0 + 4], sacc[kb][i0 + 5]),
                                             E::pack2(sacc[kb][i0 + 6], sacc[kb][i0 + 7])};
                         const int key0 = kb * 32 + 16 * t2;
-    #pragma unroll
+#pragma unroll
                         for (int nb = 0; nb < C::NDB; ++nb) {
                             const uint8_t *va = stage + v_addr[nb % NVA] + key0 * C::RBV + (nb / NVA) * (NVA * 64);
                             const u32x2_t a0 = lds_read_tr16(va);
@@ -919,9 +919,9 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         const int64_t grow = s.q0 + bp.row;  // token row of o
         if constexpr (!SPLIT) {
             uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * DV + 4 * g;
-    #pragma unroll
+#pragma unroll
             for (int nb = 0; nb < C::NDB; ++nb) {
-    #pragma unroll
+#pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const f32x16_t &a = oacc[nb];
                     *(u32x2_t *)(op + nb * 32 + 8 * i4) =
@@ -941,9 +941,9 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             // by this split's own sum; the combine pass reweights by the LSEs)
             const int64_t prow = ((int64_t)bp.it.sp * p.total_rows + grow) * p.H + h;
             float *pp = p.part_o + prow * DV + 4 * g;
-    #pragma unroll
+#pragma unroll
             for (int nb = 0; nb < C::NDB; ++nb) {
-    #pragma unroll
+#pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const f32x16_t &a = oacc[nb];
                     *(f32x4_t *)(pp + nb * 32 + 8 * i4) =
@@ -1157,6 +1157,31 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(KernelParams p)
         nq = imin((S_q + BM - 1) / BM, p.num_qt);
         cost = (float)nq * (float)S_kv;
     };
+    if (K <= kPlanThreads) {
+        // one pair per lane: its position in the order is the number of pairs
+        // before it, and its first entry the items of those pairs
+        int nq = 0;
+        float c = -1.0f;
+        if (t < K) pair(t, nq, c);
+        const int items = nq * p.num_splits;
+        int e = 0, total = 0;
+        for (int j = 0; j < K; ++j) {
+            const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), j));
+            const int ij = __builtin_amdgcn_readlane(items, j);
+            e += (cj > c || (cj == c && j < t)) ? ij : 0;
+            total += ij;
+        }
+        const int bh = x + 8 * t;
+        for (int qt = nq - 1; qt >= 0; --qt)
+            for (int sp = 0; sp < p.num_splits; ++sp)
+                list[e++] = (uint64_t)(uint32_t)bh | (uint64_t)(uint32_t)(qt << 8 | sp) << 32;
+        for (uint32_t i = (uint32_t)total + t; i < per_queue; i += kPlanThreads) list[i] = 0xffffffffu;
+        if (t == 0) {
+            p.queue[x] = 0;
+            p.queue[kQueueCount + x] = (uint32_t)total;
+        }
+        return;
+    }
     const bool sorted = K <= kPlanSortPairs;
     if (sorted) {
         int n = 1;

@@ -117,3 +117,19 @@ def test_persistent_schedule_in_a_graph():
         _same((out,), (eager,), f"replay {r}")
         dev.forward(schedule=2)  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("batch,nhead", [(200, 4), (4200, 4)])
+def test_many_pairs(batch, nhead):
+    # more (b, h) pairs per XCD queue than one wave ranks (100: the bitonic sort
+    # in LDS) and than are sorted at all (2100: the pairs keep their order)
+    import numpy as np
+    rng = np.random.default_rng(batch)
+    U = rng.integers(0, 200 if batch < 1000 else 6, size=batch, endpoint=True)
+    T = rng.integers(0, 3, size=batch, endpoint=True)
+    w = W.build(f"pairs{batch}", dtype="bf16", batch=batch, nhead=nhead, hdim_qk=64, hdim_v=64,
+                jagged=True, cross=False, causal=True, softmax=False, alpha=0.0,
+                groups=[W.MaskGroup(0, 2, 0, 0.0)], uih_q=U, targets=T, seed=batch)
+    print(f"case pairs{batch}", flush=True)
+    a, b = _both(DeviceInputs(w))
+    _same(a, b, w.name)
