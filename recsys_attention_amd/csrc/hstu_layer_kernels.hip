@@ -558,13 +558,15 @@ static int device_cus() {
     return n;
 }
 
-// Persistent 256 x 256 tiles when there are at least four per CU (and K is a
+// Persistent 256 x 256 tiles when there are at least two per CU (and K is a
 // multiple of their 32-wide k-tiles), else 128 x 128 tiles, two work-groups per CU.
+// (The layer's f2, 83302 x 512 x 512 with the residual: 82 us persistent against
+// 91 us with 128 x 128 tiles; 64 x 256 tiles: 96 us.)
 template <int DT>
 static hipError_t launch_linear_dt(const LinearParams &p, hipStream_t stream) {
     const int cus = device_cus();
     const int64_t big = ((p.M + kPBM - 1) / kPBM) * ((p.N + kPBN - 1) / kPBN);
-    if (cus >= 8 && big >= 4 * (int64_t)cus && p.K % kPBK == 0) return launch_linear_persistent<DT>(p, cus, stream);
+    if (cus >= 8 && big >= 2 * (int64_t)cus && p.K % kPBK == 0) return launch_linear_persistent<DT>(p, cus, stream);
     return launch_linear_tile<DT, 128, 128>(p, stream);
 }
 

@@ -38,9 +38,12 @@ LINEAR_CASES = [
     (1000, 512, 136, "bf16", "none", True, 64),
     (4133, 1024, 512, "bf16", "silu", False, 8),
     (300, 256, 520, "fp16", "silu", True, 0),
-    # enough rows for the 256 x 256 tiles (>= 1024 of them), ragged in M
+    # enough rows for the persistent 256 x 256 tiles (two per CU: >= 512 of them),
+    # ragged in M
     (33001, 512, 2048, "bf16", "silu", False, 0),
     (33001, 512, 2048, "fp16", "none", True, 8),
+    # the layer's f2 shape class: two column tiles, residual (548 tiles)
+    (70001, 512, 512, "bf16", "none", True, 0),
     # persistent kernel with fewer k-steps per tile than its prefetch depth, 7 column tiles
     (40000, 64, 1792, "bf16", "silu", True, 0),
 ]
