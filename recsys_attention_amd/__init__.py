@@ -204,7 +204,7 @@ def hstu_fwd(q, k, v, *, seq_offsets=None, seq_offsets_kv=None, num_targets=None
     with rab_time float32 [H, 11] (time-gap buckets), rab_pos float32 [H, P]
     (positional, indexed by min(|i - j|, P - 1)).
     schedule 0 and 3 use a small workspace (uint8 device tensor of workspace_size(...,
-    num_splits=1) bytes) for the persistent schedule's work counters; it is allocated
+    num_splits=1) bytes) for the persistent schedule's work queues; it is allocated
     when not given."""
     lib = _abi.load()
     c = _Call(q, k, v, seq_offsets=seq_offsets, seq_offsets_kv=seq_offsets_kv,

@@ -169,7 +169,7 @@ void fill_params(const hstu_fwd_args_t *a, int32_t num_splits, hstu::KernelParam
 }
 
 // Workspace layout: split-KV partial outputs (256-byte aligned), their LSEs
-// (softmax), then, for the persistent schedule, the work counters.
+// (softmax), then, for the persistent schedule, the work queues.
 size_t partial_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     if (num_splits <= 1) return 0;
     const size_t rows = (size_t)rows_q(a) * (size_t)a->nhead * (size_t)num_splits;

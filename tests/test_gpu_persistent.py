@@ -1,8 +1,9 @@
-"""The persistent schedule (3: a resident grid taking work items from per-XCD
-queues) against the one-work-group-per-item schedule (2).  Both run the same
-per-item code on the same item order, so their outputs must agree bit for bit;
-the other GPU tests compare the default schedule (3 when the workspace is
-given, which the binding does) with the oracle."""
+"""The persistent schedule (3: a resident grid taking work items from planned
+per-XCD queues) against the one-work-group-per-item schedule (2).  Both run the
+same per-item code on the same items (in different orders, and no item's result
+depends on another's), so their outputs must agree bit for bit.  The other GPU
+tests compare the default schedule with the oracle: 3 for grids of at least
+2048 possible items (the binding provides the workspace), 2 below."""
 import pytest
 import torch
 
