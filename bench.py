@@ -305,6 +305,17 @@ def layer_main(args, torch):
     print(json.dumps(out_line), flush=True)
 
 
+def schedule_run(w, splits, schedule):
+    """The work order the library picks for schedule 0 (its rule: the persistent
+    grid, 3, from 2048 possible items when the workspace holds the queues, which
+    the binding provides; else the per-item grid, 2)."""
+    if schedule != 0:
+        return schedule
+    bh_pad = (w.batch * w.nhead + 7) // 8 * 8
+    items = bh_pad * ((w.max_seqlen_q + 127) // 128) * splits
+    return 3 if items >= 2048 else 2
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -373,6 +384,7 @@ def main():
                    "hdim_qk": w.hdim_qk, "hdim_v": w.hdim_v, "total_tokens": w.total_q,
                    "max_seqlen": w.max_seqlen_q, "visible_pairs": pairs,
                    "splits": splits, "schedule": args.schedule,
+                   "schedule_run": schedule_run(w, splits, args.schedule),
                    "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)},
         "roofline": roofline(w, splits, tflops, ms, traffic, rab),
         "device": device_info(torch),
