@@ -134,3 +134,29 @@ def test_many_pairs(batch, nhead):
     print(f"case pairs{batch}", flush=True)
     a, b = _both(DeviceInputs(w))
     _same(a, b, w.name)
+
+
+def test_two_streams_at_once():
+    # calls that overlap in time, each with its own workspace, do not interfere
+    import recsys_attention_amd as hip
+    w1 = W.config("jagged_silu_bf16_d128_causal_long")
+    w2 = W.build("streams2", dtype="bf16", batch=16, nhead=8, hdim_qk=128, hdim_v=128, jagged=True,
+                 cross=False, causal=True, softmax=False, alpha=0.0,
+                 groups=[W.MaskGroup(0, 6, 0, 0.0)], uih_q=[1500 + 97 * i for i in range(16)],
+                 targets=[3] * 16, seed=77)
+    d1, d2 = DeviceInputs(w1), DeviceInputs(w2)
+    ref1, ref2 = d1.forward(schedule=2), d2.forward(schedule=2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    print("case two streams", flush=True)
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            o1 = hip.hstu_fwd(d1.q, d1.k, d1.v, schedule=3, **d1.kw)
+        with torch.cuda.stream(s2):
+            o2 = hip.hstu_fwd(d2.q, d2.k, d2.v, schedule=3, **d2.kw)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        _same((o1,), (ref1,), "stream 1")
+        _same((o2,), (ref2,), "stream 2")
