@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "hstu_launch.h"
 #include "hstu_plan.h"
@@ -768,11 +769,26 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         wait_all_loads();
         __syncthreads();
 
+        // Runs step(n, stage) on tiles n, n + 1, ... while more(n) holds.  Tile n
+        // uses ring stage n & 1, passed as a template constant: each step body
+        // exists once per stage, so the stage sits in the immediate offsets of the
+        // LDS reads instead of costing address instructions on every tile.
+        auto run_tiles = [&](int &n, auto &&more, auto &&step) {
+            while (more(n)) {
+                if ((n & 1) == 0) {
+                    step(n, std::integral_constant<int, 0>{});
+                    if (!more(++n)) break;
+                }
+                step(n, std::integral_constant<int, 1>{});
+                ++n;
+            }
+        };
+
         // one key tile through the generic body (any mask, any variant)
-        auto generic_step = [&](int n) {
+        auto generic_step = [&](int n, auto stage_const) {
+            constexpr int buf = decltype(stage_const)::value;
             if (n == ntiles - 2) reserve_next();
             if (n == ntiles - 1) fetch_next();
-            const int buf = n & 1;
             const bool has_next = n + 1 < ntiles;
             // after the last tile the loads fall past the sequence's buffer range: they
             // return zeros into the free stage without touching memory, so no load
@@ -886,10 +902,10 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             // generic body.  (Choosing between the two bodies per tile inside one loop
             // made the compiler copy the 64 output accumulators between two register
             // sets on every tile.)
-            auto full_step = [&](int n) {
+            auto full_step = [&](int n, auto stage_const) {
+                constexpr int buf = decltype(stage_const)::value;
                 if (n == ntiles - 2) reserve_next();
                 if (n == ntiles - 1) fetch_next();
-                const int buf = n & 1;
                 const int t_next = n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
                 silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
                                           [&](int idx) {
@@ -898,13 +914,16 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 wait_all_loads_here();
                 __syncthreads();
             };
+            auto full = [&](int n) { return n < ntiles && bp.tile_full(bp.tiles.at(n) * BN, BN); };
+            auto mixed = [&](int n) { return n < ntiles && !bp.tile_full(bp.tiles.at(n) * BN, BN); };
             int n = 0;
             while (n < ntiles) {
-                for (; n < ntiles && !bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) generic_step(n);
-                for (; n < ntiles && bp.tile_full(bp.tiles.at(n) * BN, BN); ++n) full_step(n);
+                run_tiles(n, mixed, generic_step);
+                run_tiles(n, full, full_step);
             }
         } else {
-            for (int n = 0; n < ntiles; ++n) generic_step(n);
+            int n = 0;
+            run_tiles(n, [&](int n) { return n < ntiles; }, generic_step);
         }
 
         // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
