@@ -151,6 +151,7 @@ void fill_params(const hstu_fwd_args_t *a, int32_t num_splits, hstu::KernelParam
     p.num_splits = num_splits;
     p.schedule = a->schedule == 0 ? 2 : a->schedule;
     p.alpha = a->alpha != 0.0f ? a->alpha : (float)(1.0 / sqrt((double)a->hdim_qk));
+    p.inv_alpha = (float)(1.0 / (double)p.alpha);
     p.rab_ts = a->rab_timestamps;
     p.rab_time = a->rab_timestamps ? a->rab_time : nullptr;
     p.rab_pos = a->rab_pos;

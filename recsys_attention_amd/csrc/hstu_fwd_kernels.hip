@@ -346,13 +346,14 @@ __device__ __forceinline__ int32_t wave_max_dpp(int32_t x) {
                 imax(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
-// Element-wise bias of one 32-key block of raw scores x = q.k of this lane's row
-// -> the biased score in the non-linearity's domain:
-//   x <- ac x + pos[min(|row - j|, pmax)] + time[bucket(|t_row - t_j|)].
+// Bias of one 32-key block of this lane's row, divided by alpha, as the initial
+// accumulator of the block's score MFMAs:
+//   x <- (pos[min(|row - j|, pmax)] + time[bucket(|t_row - t_j|)]) / alpha,
+// so the MFMAs leave q.k + b / alpha and alpha times that is the biased score
+// alpha q.k + b; from there the path is the one without bias.
 // Element i is key key0 + 8(i/4) + i%4; ts4 points at that key0's timestamp in
-// the LDS copy of the tile's key timestamps (16-byte aligned).  The tables hold
-// the bias as given (softmax takes the biased score to the log2 domain after).
-__device__ __forceinline__ void rab_block(f32x16_t &x, float ac, int row, int key0, const float *pos,
+// the LDS copy of the tile's key timestamps (16-byte aligned).
+__device__ __forceinline__ void rab_block(f32x16_t &x, float inv_a, int row, int key0, const float *pos,
                                           int pmax, const int32_t *ts4, int32_t t_row, const u32x4_t *oct,
                                           bool has_pos, bool has_time) {
 #pragma unroll
@@ -368,13 +369,14 @@ __device__ __forceinline__ void rab_block(f32x16_t &x, float ac, int row, int ke
                 b = pos[imin(row > j ? row - j : j - row, pmax)];
             }
             if (has_time) b += rab_time_value(abs_gap(t_row, tk[e]), oct);
-            x[i] = fmaf(x[i], ac, b);
+            x[i] = b * inv_a;
         }
     }
 }
 
-// The bias of one key tile (keys j0 .. j0 + BN - 1) for this lane's row, with the
-// two terms taken per tile where the tile allows it:
+// The bias of one key tile (keys j0 .. j0 + BN - 1) for this lane's row, divided
+// by alpha, as the initial accumulator of the tile's score MFMAs (see
+// rab_block), with the two terms taken per tile where the tile allows it:
 //  * time: the tile's smallest and largest key timestamps bound every gap of the
 //    row; when both bounds fall into one bucket (for every row of the wave), the
 //    time term is one value per row for the whole tile;
@@ -386,7 +388,7 @@ __device__ __forceinline__ void rab_block(f32x16_t &x, float ac, int row, int ke
 // Other tiles (the diagonal, gaps across a bucket edge) go element by element.
 // Element (kb, i) is key j0 + 32 kb + 4 g + c with c = 8(i/4) + i%4.
 template <int NKB, int BN>
-__device__ __forceinline__ void rab_tile(f32x16_t *x, float ac, int row, int j0, int g, int wrow0,
+__device__ __forceinline__ void rab_tile(f32x16_t *x, float inv_a, int row, int j0, int g, int wrow0,
                                          const float *pos, int P, const int32_t *ts, int32_t t_row,
                                          bool row_valid, int32_t S_kv, const u32x4_t *oct, bool has_pos,
                                          bool has_time, int lane) {
@@ -423,10 +425,11 @@ __device__ __forceinline__ void rab_tile(f32x16_t *x, float ac, int row, int j0,
     if (!time_tile) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-            rab_block(x[kb], ac, row, j0 + kb * 32 + 4 * g, pos, P - 1, ts + kb * 32 + 4 * g, t_row, oct,
+            rab_block(x[kb], inv_a, row, j0 + kb * 32 + 4 * g, pos, P - 1, ts + kb * 32 + 4 * g, t_row, oct,
                       has_pos, has_time);
         return;
     }
+    const float tva = tv * inv_a;
     if (has_pos && wrow0 - j0 >= BN - 1) {
         // below: index row - j = (row - j0) - 4g - c, read at base + (BN - 5 - c) >= 0
         const int base = imin(row - j0, P + BN - 2) - 4 * g - (BN - 5);
@@ -435,7 +438,7 @@ __device__ __forceinline__ void rab_tile(f32x16_t *x, float ac, int row, int j0,
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int c = 32 * kb + 8 * (i >> 2) + (i & 3);
-                x[kb][i] = fmaf(x[kb][i], ac, pos[base + (BN - 5 - c)] + tv);
+                x[kb][i] = fmaf(pos[base + (BN - 5 - c)], inv_a, tva);
             }
     } else if (has_pos && wrow0 + 31 < j0) {
         // above: index j - row = (j0 - row) + 4g + c
@@ -445,7 +448,7 @@ __device__ __forceinline__ void rab_tile(f32x16_t *x, float ac, int row, int j0,
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int c = 32 * kb + 8 * (i >> 2) + (i & 3);
-                x[kb][i] = fmaf(x[kb][i], ac, pos[base + c] + tv);
+                x[kb][i] = fmaf(pos[base + c], inv_a, tva);
             }
     } else if (has_pos) {
 #pragma unroll
@@ -453,13 +456,13 @@ __device__ __forceinline__ void rab_tile(f32x16_t *x, float ac, int row, int j0,
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int j = j0 + 32 * kb + 4 * g + 8 * (i >> 2) + (i & 3);
-                x[kb][i] = fmaf(x[kb][i], ac, pos[imin(row > j ? row - j : j - row, P - 1)] + tv);
+                x[kb][i] = fmaf(pos[imin(row > j ? row - j : j - row, P - 1)], inv_a, tva);
             }
     } else {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[kb][i] = fmaf(x[kb][i], ac, tv);
+            for (int i = 0; i < 16; ++i) x[kb][i] = tva;
     }
 }
 
@@ -484,6 +487,7 @@ template <class E, int D, class IssueLoad>
 __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const uint32_t *k_addr,
                                                     const uint32_t *v_addr, const u32x4_t *qreg,
                                                     f32x16_t *oacc, float neg_alpha_log2e,
+                                                    const f32x16_t &init0, const f32x16_t &init1,
                                                     IssueLoad &&issue_load) {
     using C = Tile<D, 64>;
     static_assert(C::NKB == 2 && C::KSTEPS == 8 && C::NDB == 4, "hdim 128, 64-key tiles");
@@ -503,7 +507,7 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
                        E::pack2(x[i0 + 4], x[i0 + 5]), E::pack2(x[i0 + 6], x[i0 + 7])};
     };
 
-    f32x16_t s0 = {}, s1 = {};
+    f32x16_t s0 = init0, s1 = init1;
     u32x4_t op0[8], op1[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) op0[kk] = kread(0, kk);
@@ -547,9 +551,9 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
 }
 
 // RAB: relative attention bias.  The bias is added to alpha q.k before the mask
-// and the non-linearity, so in that variant the scores carry alpha themselves
-// (SiLU of the biased score, epilogue without alpha) instead of folding it into
-// the exponent and the epilogue.
+// and the non-linearity; it enters as the score MFMAs' initial accumulator,
+// divided by alpha (rab_tile), so the scores, the non-linearity and the epilogue
+// are those of the variant without bias.
 template <int DT, int D, bool SOFTMAX, bool SPLIT, int DV = D, bool RAB = false>
 __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2))) void hstu_fwd_kernel(KernelParams p) {
     constexpr int BN = key_tile_for(D);
@@ -754,15 +758,14 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] = f32x16_t{};
         float m_run = -INFINITY, l_run = 0.f;
-        // with the bias the scores already carry alpha (rab_block)
-        const float neg_alpha_log2e = RAB ? -kLog2e : -p.alpha * kLog2e;
-        const float sc_soft = RAB ? kLog2e : p.alpha * kLog2e;
+        const float neg_alpha_log2e = -p.alpha * kLog2e;
+        const float sc_soft = p.alpha * kLog2e;
         // the bias's scalars, held in registers: re-read from the (re-read per
         // item) arguments inside the tile loop, their loads each waited for the
         // outstanding LDS reads too (a scalar-memory wait)
-        float rab_alpha = p.alpha;
+        float rab_inv_alpha = p.inv_alpha;
         int32_t rab_pos_len = p.rab_pos_len;
-        if constexpr (RAB) asm volatile("" : "+s"(rab_alpha), "+s"(rab_pos_len));
+        if constexpr (RAB) asm volatile("" : "+s"(rab_inv_alpha), "+s"(rab_pos_len));
         const uint8_t *lds0 = &lds[0][0];
 
         if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
@@ -807,8 +810,14 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 __builtin_amdgcn_s_setprio(1);
                 // ---- S^T = K Q^T, the key blocks' MFMA chains interleaved
                 f32x16_t sacc[C::NKB];
+                if constexpr (RAB) {
+                    rab_tile<C::NKB, BN>(sacc, rab_inv_alpha, bp.row, j0, g, wrow0, pos_lds, rab_pos_len,
+                                         ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
+                                         has_time, lane);
+                } else {
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16_t{};
+                    for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16_t{};
+                }
 #pragma unroll
                 for (int kk = 0; kk < C::KSTEPS; ++kk) {
 #pragma unroll
@@ -820,10 +829,6 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
                 // ---- mask + non-linearity; element i of block kb is key
                 //      j0 + 32*kb + 8*(i/4) + 4*g + i%4 of this lane's row
-                if constexpr (RAB)
-                    rab_tile<C::NKB, BN>(sacc, rab_alpha, bp.row, j0, g, wrow0, pos_lds, rab_pos_len,
-                                         ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
-                                         has_time, lane);
                 if constexpr (!SOFTMAX) {
                     // p = x sigmoid(alpha x); the factor alpha of SiLU(alpha x) goes into the epilogue
                     if (wave_mask) {
@@ -896,7 +901,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             wait_all_loads_here();
             __syncthreads();
         };
-        if constexpr (!SOFTMAX && !RAB && D == 128 && DV == 128) {
+        if constexpr (!SOFTMAX && D == 128 && DV == 128) {
             // Tiles visible to every valid row of the work-group run through the
             // software-pipelined body, in a loop of their own; the others through the
             // generic body.  (Choosing between the two bodies per tile inside one loop
@@ -907,8 +912,15 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 if (n == ntiles - 2) reserve_next();
                 if (n == ntiles - 1) fetch_next();
                 const int t_next = n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
+                f32x16_t init[2] = {};
+                if constexpr (RAB) {
+                    rab_tile<2, BN>(init, rab_inv_alpha, bp.row, bp.tiles.at(n) * BN, g, wrow0, pos_lds,
+                                    rab_pos_len, ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
+                                    has_time, lane);
+                    issue_ts(t_next, buf ^ 1);
+                }
                 silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
-                                          [&](int idx) {
+                                          init[0], init[1], [&](int idx) {
                                               if (idx < LPT) issue_one(t_next, buf ^ 1, idx);
                                           });
                 wait_all_loads_here();
@@ -927,7 +939,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         }
 
         // ---- epilogue: lane holds columns 32nb + 8(i/4) + 4g + i%4 of its row
-        float scale = RAB ? s.attn_scale : s.attn_scale * p.alpha;
+        float scale = s.attn_scale * p.alpha;
         float lse_val = 0.f;
         if constexpr (SOFTMAX) {
             const float l = l_run + __shfl_xor(l_run, 32);

@@ -31,6 +31,7 @@ struct KernelParams {
     int32_t num_splits;
     int32_t schedule;             // 1 or 2 (see decode_work)
     float alpha;                  // resolved QK scale
+    float inv_alpha;              // 1 / alpha (the bias enters the score MFMAs divided by alpha)
     int32_t G, per_group;
     GroupDev groups[HSTU_MAX_GROUPS];
     // relative attention bias (nullptr: term absent)
