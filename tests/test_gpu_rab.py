@@ -121,3 +121,26 @@ def test_bias_named_workload_sampled_rows():
                                pos_table=rab.pos_table)
     toks = np.asarray(w.q_offsets)[bs] + ids
     compare(got[toks, hs], o_ref, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("d,dv,softmax", [(128, 128, False), (128, 128, True), (64, 64, False), (256, 256, True)])
+def test_zero_bias_tables_match_no_bias_bitwise(d, dv, softmax):
+    """All-zero tables (both terms present) give bit for bit the output without
+    bias: the bias enters the score MFMAs as their initial accumulator (divided by
+    alpha), so zero tables leave every later step identical.  Long causal rows so
+    that the d=128 SiLU case runs full key tiles through the pipelined body."""
+    groups = [W.MaskGroup(0, 6, 0, 0.0)]
+    w = W.build("bias_zero", dtype="bf16", batch=3, nhead=2, hdim_qk=d, hdim_v=dv, jagged=True,
+                cross=False, causal=True, softmax=softmax, alpha=0.0, groups=groups,
+                uih_q=[1500, 333, 70], targets=[7, 0, 3], seed=71)
+    rab = W.rab_inputs(w, 73, pos_len=512)
+    rab = W.RabInputs(rab.timestamps, np.zeros_like(rab.time_table), np.zeros_like(rab.pos_table))
+    _log(f"case zero tables: d={d}/{dv} softmax={softmax}")
+    dev = DeviceInputs(w)
+    a = dev.forward(rab=rab)
+    b = dev.forward()
+    torch.cuda.synchronize()
+    if softmax:
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    else:
+        assert torch.equal(a, b)
