@@ -144,3 +144,16 @@ def test_zero_bias_tables_match_no_bias_bitwise(d, dv, softmax):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     else:
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("alpha,softmax", [(0.37, False), (-0.05, False), (0.37, True), (-0.05, True)])
+def test_bias_explicit_alpha(alpha, softmax):
+    """Explicit alpha, positive and negative: the bias enters the score MFMAs
+    divided by alpha (1/alpha computed on the host), and alpha times the sum is
+    the biased score, whatever alpha's sign.  Rows long enough for full key tiles
+    (the pipelined body at hdim 128 with SiLU)."""
+    groups = [W.MaskGroup(0, 6, 0, 0.0)]
+    w = W.build("bias_alpha", dtype="bf16", batch=2, nhead=2, hdim_qk=128, hdim_v=128, jagged=True,
+                cross=False, causal=True, softmax=softmax, alpha=alpha, groups=groups,
+                uih_q=[900, 211], targets=[5, 2], seed=83)
+    _check(w, W.rab_inputs(w, 89, pos_len=256, shuffle=True))
