@@ -482,6 +482,9 @@ __device__ __forceinline__ float silu_raw(float v, float neg_alpha_log2e) {
 //   C: block 0 P.V    (8 MFMAs)            + block 1 SiLU (2 scores/step) + block 1 V^T reads
 //   D: block 1 P.V    (8 MFMAs)
 // The next tile's global->LDS loads (issue_load(0..7)) are spread over phase A.
+// Inside each step sched_group_barrier puts the MFMA first (mask 0x008), then
+// the step's LDS reads (0x100), then its VALU work (0x002), so the matrix pipe
+// is fed before the SiLU arithmetic of the same step.
 // The fences change the instruction order only, never the arithmetic.
 template <class E, int D, class IssueLoad>
 __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const uint32_t *k_addr,
@@ -522,6 +525,8 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
         s0 = E::mfma(op0[kk], qreg[kk], s0);
         op1[kk] = kread(1, kk);
         issue_load(kk);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     // B
@@ -531,6 +536,9 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
         op0[kk] = vread(0, kk);
         s0[2 * kk] = silu_raw(s0[2 * kk], neg_alpha_log2e);
         s0[2 * kk + 1] = silu_raw(s0[2 * kk + 1], neg_alpha_log2e);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     const u32x4_t p0[2] = {pack8(s0, 0), pack8(s0, 8)};
@@ -541,6 +549,9 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
         op1[i] = vread(1, i);
         s1[2 * i] = silu_raw(s1[2 * i], neg_alpha_log2e);
         s1[2 * i + 1] = silu_raw(s1[2 * i + 1], neg_alpha_log2e);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     const u32x4_t p1[2] = {pack8(s1, 0), pack8(s1, 8)};
