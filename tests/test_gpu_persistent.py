@@ -160,3 +160,59 @@ def test_two_streams_at_once():
     for o1, o2 in outs:
         _same((o1,), (ref1,), "stream 1")
         _same((o2,), (ref2,), "stream 2")
+
+
+def _expected_queues(w, per_queue):
+    """The planning kernel's contract, written out: queue x holds the (b, h) pairs
+    with b*H + h = x (mod 8), longest first (cost = q-tiles x keys, ties by pair
+    index; in natural order when a queue has more than 2048 pairs), each pair's
+    q-tiles from the last to the first, then "no item" entries."""
+    import numpy as np
+    off = np.asarray(w.q_offsets, dtype=np.int64)
+    lens = off[1:] - off[:-1]
+    BH = w.batch * w.nhead
+    bh_pad = (BH + 7) // 8 * 8
+    queues, counts = [], []
+    for x in range(8):
+        pairs = []
+        for k in range((bh_pad - x + 7) // 8):
+            bh = x + 8 * k
+            if bh >= BH:
+                continue
+            S = int(lens[bh // w.nhead])
+            nq = (S + 127) // 128
+            pairs.append((k, bh, nq, float(np.float32(nq) * np.float32(S))))
+        if bh_pad // 8 <= 2048:
+            pairs.sort(key=lambda t: (-t[3], t[0]))
+        ent = [bh | (qt << 8) << 32 for _, bh, nq, _ in pairs for qt in range(nq - 1, -1, -1)]
+        counts.append(len(ent))
+        queues.append(np.array(ent + [0xFFFFFFFF] * (per_queue - len(ent)), dtype=np.uint64))
+    return queues, counts
+
+
+@pytest.mark.parametrize("batch,nhead,maxlen", [(7, 3, 700), (32, 8, 3000), (200, 4, 300), (4200, 4, 6)])
+def test_planned_queues_hold_every_item_once_in_order(batch, nhead, maxlen):
+    # the queues the planning kernel leaves in the workspace, entry by entry
+    # (the forward kernel only advances the take counters in the header)
+    import numpy as np
+    import recsys_attention_amd as hip
+    rng = np.random.default_rng(batch + nhead)
+    U = rng.integers(0, maxlen, size=batch, endpoint=True)
+    T = rng.integers(0, 3, size=batch, endpoint=True)
+    w = W.build(f"queues{batch}", dtype="bf16", batch=batch, nhead=nhead, hdim_qk=64, hdim_v=64,
+                jagged=True, cross=False, causal=True, softmax=False, alpha=0.0,
+                groups=[W.MaskGroup(0, 2, 0, 0.0)], uih_q=U, targets=T, seed=batch)
+    dev = DeviceInputs(w)
+    need = hip.workspace_size(dev.q, dev.k, dev.v, 1, **dev.kw)
+    ws = torch.full((need,), 0x5a, dtype=torch.uint8, device="cuda")
+    print(f"case queues{batch}x{nhead}", flush=True)
+    hip.hstu_fwd(dev.q, dev.k, dev.v, schedule=3, workspace=ws, **dev.kw)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    header = raw[:256].view(np.uint32)
+    per_queue = (need - 256) // 64
+    lists = raw[256:256 + 64 * per_queue].view(np.uint64).reshape(8, per_queue)
+    queues, counts = _expected_queues(w, per_queue)
+    for x in range(8):
+        assert int(header[8 + x]) == counts[x], f"queue {x} count"
+        assert np.array_equal(lists[x], queues[x]), f"queue {x} entries"
