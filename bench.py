@@ -8,8 +8,10 @@ the timed kernels; inputs are resident in HBM before timing starts.
                     [--rab none|pos|time|both]
 
 Prints one JSON line: effective TFLOP/s counting 2 * (hdim_qk + hdim_v) FLOPs
-per visible (b, h, i, j) pair, the roofline of the dominant kernel, and the CPU
-oracle timed on a bounded sample of the same workload.
+per visible (b, h, i, j) pair over the median of the per-step HIP-event times
+(minimum, mean and the shader clock are logged beside it), the roofline of the
+dominant kernel, and the CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -52,6 +54,66 @@ def device_info(torch) -> dict:
     return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count}
 
 
+def sclk_reader(torch):
+    """A function returning the shader clock (MHz) the driver reports as current for
+    cuda:0 (sysfs pp_dpm_sclk of its PCI device), or None where it is not readable."""
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        path = (f"/sys/bus/pci/devices/{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:"
+                f"{pr.pci_device_id:02x}.0/pp_dpm_sclk")
+        open(path).read()
+    except (OSError, AttributeError):
+        return lambda: None
+
+    def read():
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return int("".join(c for c in line.split(":", 1)[1] if c.isdigit()))
+        except (OSError, ValueError, IndexError):
+            pass
+        return None
+    return read
+
+
+def timed_steps(torch, step, steps: int, warmup: int, warmup_s: float, stream):
+    """W warm-up steps, then more until warmup_s seconds of back-to-back launches
+    have passed (the first launches after idle run at a lower clock), then exactly
+    `steps` steps with a HIP event pair around each one, on the launch stream,
+    bracketed by device synchronisations.  The shader clock is sampled while the
+    timed steps run.  Returns per-step milliseconds and a record of the run."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    extra, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < warmup_s:
+        for _ in range(20):
+            step()
+        extra += 20
+        torch.cuda.synchronize()
+    read_clock = sclk_reader(torch)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    clocks = [read_clock()]
+    torch.cuda.synchronize()
+    clocks.append(read_clock())
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    per_sorted = sorted(per)
+    med = per_sorted[steps // 2] if steps % 2 else 0.5 * (per_sorted[steps // 2 - 1] + per_sorted[steps // 2])
+    rec = {"ms_median": round(med, 4), "ms_min": round(per_sorted[0], 4),
+           "ms_mean": round(sum(per) / steps, 4), "ms_max": round(per_sorted[-1], 4),
+           "ms_total_timed": round(evs[0].elapsed_time(evs[-1]), 4),
+           "warmup_extra_steps": extra, "warmup_s": warmup_s,
+           "sclk_mhz_during": clocks[0], "sclk_mhz_after": clocks[1], "wall_s_timed": round(wall, 3)}
+    return med, rec
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -62,10 +124,11 @@ def kernel_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the kernel takes ~1 ms: the default warm-up (~50 ms of back-to-back launches)
-    # lets the GPU clock settle, which the first few launches show they need
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-s", type=float, default=1.0,
+                    help="after the --warmup steps, keep warming up until this many seconds "
+                         "of back-to-back launches have passed (clock ramp)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
@@ -252,18 +315,7 @@ def layer_main(args, torch):
         ("linear_f2_residual", lambda: hip.hstu_linear(ao, w2, b2, residual=x, out=out),
          2.0 * n * hv * d_model, 2 * (n * hv + hv * d_model + 2 * n * d_model)),
     ]
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, timing = timed_steps(torch, step, args.steps, args.warmup, args.warmup_s, stream)
     # per-kernel durations: events between the four launches of each step
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
     for e in evs:
@@ -298,7 +350,7 @@ def layer_main(args, torch):
                    "pct_of_bf16_peak": round(100.0 * tflops / PEAK_TFLOPS[w.dtype], 2)},
         "roofline": roof,
         "device": device_info(torch),
-        "wall_s_timed": round(wall, 3),
+        "timing": timing,
     }
     if args.cpu_seconds > 0:
         out_line["cpu_baseline"] = layer_cpu_baseline(w, d_model, li, rab, args.cpu_seconds)
@@ -352,19 +404,7 @@ def main():
     def step():
         return dev.forward(num_splits=splits, schedule=args.schedule)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, timing = timed_steps(torch, step, args.steps, args.warmup, args.warmup_s, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
@@ -388,7 +428,7 @@ def main():
                    "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)},
         "roofline": roofline(w, splits, tflops, ms, traffic, rab),
         "device": device_info(torch),
-        "wall_s_timed": round(wall, 3),
+        "timing": timing,
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, rab)

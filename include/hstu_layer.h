@@ -91,9 +91,12 @@ hstu_status_t hstu_norm_gate_fwd(const hstu_norm_gate_args_t *args, void *hip_st
  * ignored (the layer uses its own buffers).  Tokens n = attn.total_q (jagged) or
  * batch * seqlen_q.  x, out [n][d_model] dense; w1 [2 H (dv + dqk)][d_model];
  * b1 [2 H (dv + dqk)]; w2 [d_model][H dv]; b2 [d_model]; ln_gamma, ln_beta [H dv]
- * or NULL.  d_model % 64 == 0, H dv <= 4096.  out must not overlap x.
+ * or NULL.  d_model % 64 == 0; H dv a multiple of 64 (the input width of f2) and
+ * <= 4096.  out must not overlap x.  Every launch's arguments are checked before
+ * the first launch, so an argument error never leaves the layer half done.
  * The workspace (hstu_layer_workspace_size bytes, 256-byte aligned) holds the
- * projection [n][2 H (dv + dqk)] and the attention output [n][H dv]. */
+ * projection [n][2 H (dv + dqk)] and the attention output [n][H dv]; with no
+ * tokens (n = 0) nothing is launched and ws may be NULL. */
 typedef struct {
     hstu_fwd_args_t attn;
     int32_t d_model;

@@ -8,9 +8,16 @@ entry point raises.
     o = hstu_fwd(q, k, v, seq_offsets=off, max_seqlen_q=S, num_targets=t,
                  groups=[HstuGroup(local_len=5, context_len=6, minfull_len=6,
                                    attn_scale=0.0, max_uih_q=870)])
+
+Every entry point takes stream= (a torch.cuda.Stream; default the current
+stream): the kernels are enqueued there and the call's own allocations (output,
+LSE, workspace) are made there, so the caching allocator reuses them in that
+stream's order.  Ordering the inputs' producers before that stream is the
+caller's part, as for any torch operation on a side stream.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import dataclasses
 from typing import Optional, Sequence
@@ -207,25 +214,31 @@ def hstu_fwd(q, k, v, *, seq_offsets=None, seq_offsets_kv=None, num_targets=None
     num_splits=1) bytes) for the persistent schedule's work queues; it is allocated
     when not given."""
     lib = _abi.load()
-    c = _Call(q, k, v, seq_offsets=seq_offsets, seq_offsets_kv=seq_offsets_kv,
-              num_targets=num_targets, max_seqlen_q=max_seqlen_q, max_seqlen_kv=max_seqlen_kv,
-              cross=cross, causal=causal, softmax=softmax, alpha=alpha, groups=groups,
-              return_lse=return_lse, out=out, schedule=schedule, rab_timestamps=rab_timestamps,
-              rab_time=rab_time, rab_pos=rab_pos)
-    ws_ptr, ws_bytes = _workspace(lib, c, 1, workspace, q.device, stream)
-    _abi.check(lib.hstu_fwd(ctypes.byref(c.args), ws_ptr, ws_bytes, c.stream(stream)))
+    with _on(stream):
+        c = _Call(q, k, v, seq_offsets=seq_offsets, seq_offsets_kv=seq_offsets_kv,
+                  num_targets=num_targets, max_seqlen_q=max_seqlen_q, max_seqlen_kv=max_seqlen_kv,
+                  cross=cross, causal=causal, softmax=softmax, alpha=alpha, groups=groups,
+                  return_lse=return_lse, out=out, schedule=schedule, rab_timestamps=rab_timestamps,
+                  rab_time=rab_time, rab_pos=rab_pos)
+        ws_ptr, ws_bytes = _workspace(lib, c, 1, workspace, q.device)
+        _abi.check(lib.hstu_fwd(ctypes.byref(c.args), ws_ptr, ws_bytes, c.stream(stream)))
     return _result(c, return_lse)
 
 
-def _workspace(lib, c, num_splits, workspace, device, stream):
-    """(pointer, bytes) of the call's workspace, allocated on the call's stream when
-    not given and the call needs one."""
+def _on(stream):
+    """Context in which a call's own allocations (output, LSE, workspace, counters) are
+    made: the caller's stream when one is given, so that the caching allocator
+    hands out and later reuses those blocks in that stream's order (the kernels
+    run there); otherwise the current stream, where they run too."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _workspace(lib, c, num_splits, workspace, device):
+    """(pointer, bytes) of the call's workspace, allocated (on the stream of the
+    enclosing _on context) when not given and the call needs one."""
     need = int(lib.hstu_fwd_workspace_size(ctypes.byref(c.args), int(num_splits)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
-        if stream is not None:
-            # the allocation belongs to the current stream; the kernels run on `stream`
-            workspace.record_stream(stream)
     if workspace is None:
         return None, 0
     c.keep_workspace = workspace
@@ -253,10 +266,11 @@ def hstu_fwd_splitkv(q, k, v, num_splits, *, workspace=None, stream=None, **kw):
     tensor of at least workspace_size() bytes) is allocated when not given."""
     lib = _abi.load()
     d = _call_kw(kw)
-    c = _Call(q, k, v, **d)
-    ws_ptr, ws_bytes = _workspace(lib, c, num_splits, workspace, q.device, stream)
-    _abi.check(lib.hstu_fwd_splitkv(ctypes.byref(c.args), int(num_splits), ws_ptr, ws_bytes,
-                                    c.stream(stream)))
+    with _on(stream):
+        c = _Call(q, k, v, **d)
+        ws_ptr, ws_bytes = _workspace(lib, c, num_splits, workspace, q.device)
+        _abi.check(lib.hstu_fwd_splitkv(ctypes.byref(c.args), int(num_splits), ws_ptr, ws_bytes,
+                                        c.stream(stream)))
     return _result(c, d["return_lse"])
 
 
@@ -264,11 +278,12 @@ def hstu_count_visible_pairs(q, k, v, *, stream=None, **kw) -> int:
     """Visible (b, h, i, j) pairs inside the key tiles the forward kernel schedules,
     counted on the device with the kernel's own predicate."""
     lib = _abi.load()
-    c = _Call(q, k, v, **_call_kw(kw))
-    cnt = torch.zeros(1, dtype=torch.int64, device=q.device)
-    _abi.check(lib.hstu_count_visible_pairs(ctypes.byref(c.args), ctypes.c_void_p(cnt.data_ptr()),
-                                            c.stream(stream)))
-    return int(cnt.item())
+    with _on(stream):
+        c = _Call(q, k, v, **_call_kw(kw))
+        cnt = torch.zeros(1, dtype=torch.int64, device=q.device)
+        _abi.check(lib.hstu_count_visible_pairs(ctypes.byref(c.args), ctypes.c_void_p(cnt.data_ptr()),
+                                                c.stream(stream)))
+        return int(cnt.item())
 
 
 # ------------------------------------------------------------- the HSTU layer
@@ -315,7 +330,8 @@ def hstu_linear(x, w, bias=None, *, activation="none", residual=None, out=None, 
             raise ValueError(f"residual must be [{M}, {N}] of x's dtype")
         rs = _rows2d(residual, "residual")
     if out is None:
-        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+        with _on(stream):
+            out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     if out.dtype != x.dtype or tuple(out.shape) != (M, N):
         raise ValueError(f"out must be [{M}, {N}] of x's dtype")
     a = _abi.LinearArgsC(dtype=dt, rows=M, in_features=K, out_features=N, x=x.data_ptr(), x_stride=xs,
@@ -335,7 +351,8 @@ def hstu_norm_gate(a, u, gamma=None, beta=None, eps=1e-6, *, out=None, stream=No
         raise ValueError("u must match a's shape and dtype")
     M, W_ = a.shape
     if out is None:
-        out = torch.empty((M, W_), dtype=a.dtype, device=a.device)
+        with _on(stream):
+            out = torch.empty((M, W_), dtype=a.dtype, device=a.device)
     if out.dtype != a.dtype or out.shape != a.shape:
         raise ValueError("out must match a's shape and dtype")
     args = _abi.NormGateArgsC(dtype=dt, rows=M, width=W_, a=a.data_ptr(), a_stride=_rows2d(a, "a"),
@@ -432,12 +449,15 @@ def hstu_layer(x, w1, b1, w2, b2, *, workspace=None, stream=None, **kw):
     The workspace (uint8 device tensor, hstu_layer_workspace_size bytes) is allocated
     when not given."""
     lib = _abi.load()
-    c = _LayerCall(x, w1, b1, w2, b2, **_layer_kw(kw))
-    need = int(lib.hstu_layer_workspace_size(ctypes.byref(c.args)))
-    if need == 0:
-        _abi.check(lib.hstu_layer_fwd(ctypes.byref(c.args), None, 0, None))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _abi.check(lib.hstu_layer_fwd(ctypes.byref(c.args), ctypes.c_void_p(workspace.data_ptr()),
-                                  workspace.numel(), _stream_ptr(x.device, stream)))
+    with _on(stream):
+        c = _LayerCall(x, w1, b1, w2, b2, **_layer_kw(kw))
+        need = int(lib.hstu_layer_workspace_size(ctypes.byref(c.args)))
+        if need == 0:
+            # invalid arguments (the call reports which) or nothing to compute
+            _abi.check(lib.hstu_layer_fwd(ctypes.byref(c.args), None, 0, _stream_ptr(x.device, stream)))
+            return c.out
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        _abi.check(lib.hstu_layer_fwd(ctypes.byref(c.args), ctypes.c_void_p(workspace.data_ptr()),
+                                      workspace.numel(), _stream_ptr(x.device, stream)))
     return c.out

@@ -109,6 +109,74 @@ struct LayerDims {
     size_t aws;  // the attention's workspace
 };
 
+// projection [n][n1], attention output [n][H dv], the attention's own workspace
+// (the persistent schedule's work queues)
+size_t layer_ws(const LayerDims &d) {
+    return align256((size_t)d.n * d.n1 * 2) + align256((size_t)d.n * d.hv * 2) + align256(d.aws);
+}
+
+// The argument blocks of the layer's four launches over the workspace ws:
+// (a) Y = SiLU(X W1^T + b1) into ws, Y = [U | V | Q | K] per token;
+// (b) the attention on views of Y (token stride n1) into A;
+// (c) Z = Norm(A) * U in place; (d) out = X + Z W2^T + b2.
+struct LayerLaunch {
+    hstu_linear_args_t f1;
+    hstu_fwd_args_t at;
+    void *aws;  // the attention's workspace
+    hstu_norm_gate_args_t ng;
+    hstu_linear_args_t f2;
+};
+
+void layer_launch_args(const hstu_layer_args_t *args, const LayerDims &d, void *ws, LayerLaunch &ll) {
+    const hstu_fwd_args_t &t = args->attn;
+    uint16_t *y1 = (uint16_t *)ws;                                            // [n][n1]: U | V | Q | K
+    uint16_t *ao = (uint16_t *)((char *)ws + align256((size_t)d.n * d.n1 * 2));  // [n][H dv]
+    ll.f1 = hstu_linear_args_t{};
+    ll.f1.dtype = t.dtype;
+    ll.f1.rows = d.n;
+    ll.f1.in_features = args->d_model;
+    ll.f1.out_features = d.n1;
+    ll.f1.x = args->x;
+    ll.f1.w = args->w1;
+    ll.f1.bias = args->b1;
+    ll.f1.activation = HSTU_ACT_SILU;
+    ll.f1.y = y1;
+
+    ll.at = t;
+    ll.at.v = y1 + d.hv;
+    ll.at.q = y1 + 2 * d.hv;
+    ll.at.k = y1 + 2 * d.hv + d.hq;
+    ll.at.q_tok_stride = ll.at.k_tok_stride = ll.at.v_tok_stride = d.n1;
+    ll.at.o = ao;
+    ll.at.o_tok_stride = d.hv;
+    ll.at.lse = nullptr;
+    ll.aws = (char *)ao + align256((size_t)d.n * d.hv * 2);
+
+    ll.ng = hstu_norm_gate_args_t{};
+    ll.ng.dtype = t.dtype;
+    ll.ng.rows = d.n;
+    ll.ng.width = d.hv;
+    ll.ng.a = ao;
+    ll.ng.u = y1;
+    ll.ng.u_stride = d.n1;
+    ll.ng.gamma = args->ln_gamma;
+    ll.ng.beta = args->ln_beta;
+    ll.ng.eps = args->ln_eps;
+    ll.ng.z = ao;
+
+    ll.f2 = hstu_linear_args_t{};
+    ll.f2.dtype = t.dtype;
+    ll.f2.rows = d.n;
+    ll.f2.in_features = d.hv;
+    ll.f2.out_features = args->d_model;
+    ll.f2.x = ao;
+    ll.f2.w = args->w2;
+    ll.f2.bias = args->b2;
+    ll.f2.activation = HSTU_ACT_NONE;
+    ll.f2.residual = args->x;
+    ll.f2.y = args->out;
+}
+
 hstu_status_t check_layer(const hstu_layer_args_t *a, LayerDims &d) {
     hstu::api::clear_error();
     if (!a) return fail(HSTU_ERR_INVALID_ARG, "args is NULL");
@@ -144,14 +212,17 @@ hstu_status_t check_layer(const hstu_layer_args_t *a, LayerDims &d) {
     if (st != HSTU_OK) return st;
     d.n = hstu::api::rows_q(&a->attn);
     d.aws = hstu_fwd_workspace_size(&t, 1);
+    // the two linear maps and the norm-gate exactly as the launches pass them
+    // (placeholder buffers as above): a shape either kernel does not take (e.g.
+    // H dv not a multiple of 64 for f2's input) fails here, before any launch
+    LayerLaunch ll;
+    layer_launch_args(a, d, (void *)base, ll);
+    if ((st = check_linear(&ll.f1)) != HSTU_OK) return st;
+    if ((st = check_norm_gate(&ll.ng)) != HSTU_OK) return st;
+    if ((st = check_linear(&ll.f2)) != HSTU_OK) return st;
     return HSTU_OK;
 }
 
-// projection [n][n1], attention output [n][H dv], the attention's own workspace
-// (the persistent schedule's work queues)
-size_t layer_ws(const LayerDims &d) {
-    return align256((size_t)d.n * d.n1 * 2) + align256((size_t)d.n * d.hv * 2) + align256(d.aws);
-}
 
 }  // namespace
 
@@ -187,66 +258,17 @@ hstu_status_t hstu_layer_fwd(const hstu_layer_args_t *args, void *ws, size_t ws_
     LayerDims d;
     hstu_status_t st = check_layer(args, d);
     if (st != HSTU_OK) return st;
+    if (d.n == 0) return HSTU_OK;  // no tokens: nothing to launch, no workspace needed
     const size_t need = layer_ws(d);
     if (!ws || ws_bytes < need)
         return fail(HSTU_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     if (((uintptr_t)ws & 255u) != 0) return fail(HSTU_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (d.n == 0) return HSTU_OK;
-    const hstu_fwd_args_t &t = args->attn;
-    uint16_t *y1 = (uint16_t *)ws;                                            // [n][n1]: U | V | Q | K
-    uint16_t *ao = (uint16_t *)((char *)ws + align256((size_t)d.n * d.n1 * 2));  // [n][H dv]
-
-    // (a) Y = SiLU(X W1^T + b1)
-    hstu_linear_args_t l1 = {};
-    l1.dtype = t.dtype;
-    l1.rows = d.n;
-    l1.in_features = args->d_model;
-    l1.out_features = d.n1;
-    l1.x = args->x;
-    l1.w = args->w1;
-    l1.bias = args->b1;
-    l1.activation = HSTU_ACT_SILU;
-    l1.y = y1;
-    if ((st = hstu_linear_fwd(&l1, hip_stream)) != HSTU_OK) return st;
-
-    // (b) the attention on views of Y (token stride n1)
-    hstu_fwd_args_t at = t;
-    at.v = y1 + d.hv;
-    at.q = y1 + 2 * d.hv;
-    at.k = y1 + 2 * d.hv + d.hq;
-    at.q_tok_stride = at.k_tok_stride = at.v_tok_stride = d.n1;
-    at.o = ao;
-    at.o_tok_stride = d.hv;
-    at.lse = nullptr;
-    void *aq = (char *)ao + align256((size_t)d.n * d.hv * 2);
-    if ((st = hstu_fwd(&at, aq, d.aws, hip_stream)) != HSTU_OK) return st;
-
-    // (c) Z = Norm(A) * U in place, then out = X + Z W2^T + b2
-    hstu_norm_gate_args_t ng = {};
-    ng.dtype = t.dtype;
-    ng.rows = d.n;
-    ng.width = d.hv;
-    ng.a = ao;
-    ng.u = y1;
-    ng.u_stride = d.n1;
-    ng.gamma = args->ln_gamma;
-    ng.beta = args->ln_beta;
-    ng.eps = args->ln_eps;
-    ng.z = ao;
-    if ((st = hstu_norm_gate_fwd(&ng, hip_stream)) != HSTU_OK) return st;
-
-    hstu_linear_args_t l2 = {};
-    l2.dtype = t.dtype;
-    l2.rows = d.n;
-    l2.in_features = d.hv;
-    l2.out_features = args->d_model;
-    l2.x = ao;
-    l2.w = args->w2;
-    l2.bias = args->b2;
-    l2.activation = HSTU_ACT_NONE;
-    l2.residual = args->x;
-    l2.y = args->out;
-    return hstu_linear_fwd(&l2, hip_stream);
+    LayerLaunch ll;
+    layer_launch_args(args, d, ws, ll);
+    if ((st = hstu_linear_fwd(&ll.f1, hip_stream)) != HSTU_OK) return st;
+    if ((st = hstu_fwd(&ll.at, ll.aws, d.aws, hip_stream)) != HSTU_OK) return st;
+    if ((st = hstu_norm_gate_fwd(&ll.ng, hip_stream)) != HSTU_OK) return st;
+    return hstu_linear_fwd(&ll.f2, hip_stream);
 }
 
 }  // extern "C"

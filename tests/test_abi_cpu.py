@@ -279,3 +279,27 @@ def test_layer_checks_the_attention_on_its_strided_views(lib):
     assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), 1 << 40,
                               None) == _abi.HSTU_ERR_UNSUPPORTED
     assert b"4 GiB" in lib.hstu_last_error()
+
+
+def test_layer_rejects_f2_width_before_any_launch(lib):
+    """One head of 96/96 makes H dv = 96, which f2 (input width a multiple of 64)
+    does not take: the layer must say so before its first launch, not after f1,
+    the attention and the norm-gate have run."""
+    attn = _args(nhead=1, hdim_qk=96, hdim_v=96)
+    a = _layer(attn)
+    assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == 0
+    assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), 1 << 30,
+                              None) == _abi.HSTU_ERR_UNSUPPORTED
+    assert b"in_features 96" in lib.hstu_last_error()
+    # three heads of 96 (H dv = 288) are refused too; four (384) are taken
+    assert lib.hstu_layer_workspace_size(ctypes.byref(_layer(_args(nhead=3, hdim_qk=96, hdim_v=96)))) == 0
+    attn4 = _args(nhead=4, hdim_qk=96, hdim_v=96)
+    assert lib.hstu_layer_workspace_size(ctypes.byref(_layer(attn4))) > 0
+
+
+def test_layer_with_no_tokens_is_a_no_op(lib):
+    """An empty problem (no sequences, no tokens) launches nothing and needs no
+    workspace."""
+    attn = _args(batch=0, total_q=0, seq_offsets_q=None, num_targets=None)
+    a = _layer(attn)
+    assert lib.hstu_layer_fwd(ctypes.byref(a), None, 0, None) == _abi.HSTU_OK

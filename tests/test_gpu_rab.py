@@ -105,22 +105,12 @@ def test_bias_schedules_agree_bitwise():
     assert torch.equal(a, b)
 
 
-def test_bias_named_workload_sampled_rows():
+def test_bias_named_workload_full():
     """The long causal workload (32 jagged sequences of 1 k - 4 k events, 8 heads,
-    d 128) with both bias terms, at full size in the benchmark's launch: sampled
-    rows against the oracle computed one row at a time."""
+    d 128) with both bias terms (2048-entry positional table), at full size in the
+    benchmark's launch: every output element against the oracle's biased forward."""
     w = W.config("jagged_silu_bf16_d128_causal_long")
-    rab = W.rab_inputs(w, 61, pos_len=2048)
-    got = o_tokens(w, DeviceInputs(w).forward(rab=rab))
-    rng = np.random.default_rng(5)
-    bs = rng.integers(0, w.batch, 48)
-    hs = rng.integers(0, w.nhead, 48)
-    ids = np.array([int(rng.integers(0, w.seqlen_q[b])) for b in bs])
-    o_ref, _ = oracle.rows_rab(oracle.problem_of(w), w.q, w.k, w.v, bs, hs, ids,
-                               timestamps=rab.timestamps, time_table=rab.time_table,
-                               pos_table=rab.pos_table)
-    toks = np.asarray(w.q_offsets)[bs] + ids
-    compare(got[toks, hs], o_ref, w.dtype, w.name)
+    _check(w, W.rab_inputs(w, 61, pos_len=2048))
 
 
 @pytest.mark.parametrize("d,dv,softmax", [(128, 128, False), (128, 128, True), (64, 64, False), (256, 256, True)])
