@@ -120,13 +120,10 @@ struct BlockPlan {
     RowSpan span;
     TileList tiles;
     int32_t row;  // row inside the sequence owned by this lane
-    // every valid row of the work-group sees all of [full_lo, full_hi] (plus the
-    // context); full_lo > full_hi when some valid row's band is empty
-    int32_t full_lo, full_hi;
+    BlockBand band;  // the work-group's rows together (union and intersection of their bands)
     // key tile [j0, j0 + BN) is visible to every valid row of the work-group
     __device__ __forceinline__ bool tile_full(int32_t j0, int32_t BN) const {
-        const int32_t j1 = j0 + BN;
-        return j1 <= s.Ck || (full_lo <= imax(j0, s.Ck) && j1 - 1 <= full_hi);
+        return block_tile_full(band, s.Ck, j0, BN);
     }
 };
 
@@ -141,36 +138,26 @@ __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, Bl
     if (r0 >= bp.s.S_q) return false;
     bp.row = r0 + wave * 32 + (lane & 31);
     bp.span = row_span(bp.s, p.causal, bp.row);
-    // union of the band parts over the work-group's rows, and their intersection
-    // over its valid rows (rows past the sequence do not constrain it)
-    int32_t lo = wave_min(bp.span.lo);
-    int32_t hi = wave_max(bp.span.hi);
-    int32_t flo = wave_max(bp.span.valid ? bp.span.lo : kEmptyHi);
-    int32_t fhi = wave_min(bp.span.valid ? bp.span.hi : kEmptyLo);
+    // the work-group's BlockBand: each row's terms (row_band) reduced over the
+    // wave, then over the waves
+    const BlockBand mine = row_band(bp.span);
+    const BlockBand wb{wave_min(mine.lo), wave_max(mine.hi), wave_max(mine.full_lo), wave_min(mine.full_hi)};
     if (lane == 0) {
-        red[4 * wave] = lo;
-        red[4 * wave + 1] = hi;
-        red[4 * wave + 2] = flo;
-        red[4 * wave + 3] = fhi;
+        red[4 * wave] = wb.lo;
+        red[4 * wave + 1] = wb.hi;
+        red[4 * wave + 2] = wb.full_lo;
+        red[4 * wave + 3] = wb.full_hi;
     }
     __syncthreads();
-    lo = red[0];
-    hi = red[1];
-    flo = red[2];
-    fhi = red[3];
+    BlockBand band = block_band_init();
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-        lo = imin(lo, red[4 * w]);
-        hi = imax(hi, red[4 * w + 1]);
-        flo = imax(flo, red[4 * w + 2]);
-        fhi = imin(fhi, red[4 * w + 3]);
-    }
-    bp.full_lo = flo;
-    bp.full_hi = fhi;
+    for (int w = 0; w < NW; ++w)
+        band = block_band_join(band, BlockBand{red[4 * w], red[4 * w + 1], red[4 * w + 2], red[4 * w + 3]});
+    bp.band = band;
     int32_t tb = 0, te = (bp.s.S_kv + BN - 1) / BN;
     if (split) split_range(bp.s.S_kv, BN, p.num_splits, bp.it.sp, &tb, &te);
     // rows r0.. exist (r0 < S_q), so the context tiles are needed
-    bp.tiles = make_tile_list(bp.s.Ck, true, lo, hi, BN, tb, te);
+    bp.tiles = make_tile_list(bp.s.Ck, true, band.lo, band.hi, BN, tb, te);
     return true;
 }
 
@@ -1133,8 +1120,14 @@ __global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D
 }
 
 // Visible pairs inside the scheduled key tiles, counted with the forward
-// kernel's own plan and predicate (the same lane -> (row, key) assignment and
-// the same full-tile shortcut).
+// kernel's own plan, lane -> (row, key) assignment and tile classes: a tile the
+// work-group-level test (BlockPlan::tile_full, which sends a tile through the
+// unmasked pipelined body) calls full counts BN keys for every valid row; a tile
+// a wave's rows classify as FULL (tile_state, the generic body's unmasked path)
+// counts BN keys per row; otherwise the predicate decides per key.  A tile the
+// work-group test calls full although one of its valid rows does not see all of
+// it adds 2^40, so that a wrong classification can never go unnoticed by an exact
+// comparison with an independently computed count of the mask's visible pairs.
 template <int BN, int NW>
 __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
     __shared__ int32_t red[4 * NW];
@@ -1146,6 +1139,10 @@ __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, uns
     for (int n = 0; n < ntiles; ++n) {
         const int j0 = bp.tiles.at(n) * BN;
         const int32_t st = tile_state(bp.span, j0, j0 + BN);
+        if (bp.tile_full(j0, BN)) {
+            if (bp.span.valid) mine += st == kTileFull ? BN / 2 : (1ull << 40);
+            continue;
+        }
         const bool wave_any = __ballot(st != kTileEmpty) != 0;
         const bool wave_mask = __ballot(bp.span.valid && st != kTileFull) != 0;
         if (!wave_any || !bp.span.valid) continue;

@@ -132,6 +132,35 @@ HSTU_HD int32_t tile_state(const RowSpan &r, int32_t j0, int32_t j1) {
     return all ? kTileFull : kTilePartial;
 }
 
+// A work-group's rows taken together (reduced over its rows in any order):
+//   lo, hi          the union of their bands (min lo, max hi; a row past the
+//                   sequence has an empty band and widens nothing);
+//   full_lo, full_hi the intersection of the bands of its valid rows (max lo,
+//                   min hi; rows past the sequence do not constrain it), empty
+//                   (full_lo > full_hi) when some valid row's band is empty.
+struct BlockBand {
+    int32_t lo, hi, full_lo, full_hi;
+};
+
+HSTU_HD BlockBand block_band_init() { return BlockBand{kEmptyLo, kEmptyHi, kEmptyHi, kEmptyLo}; }
+
+// The four terms one row contributes (combined with min, max, max, min).
+HSTU_HD BlockBand row_band(const RowSpan &r) {
+    return BlockBand{r.lo, r.hi, r.valid ? r.lo : kEmptyHi, r.valid ? r.hi : kEmptyLo};
+}
+
+HSTU_HD BlockBand block_band_join(const BlockBand &a, const BlockBand &b) {
+    return BlockBand{imin(a.lo, b.lo), imax(a.hi, b.hi), imax(a.full_lo, b.full_lo), imin(a.full_hi, b.full_hi)};
+}
+
+// Key tile [j0, j0 + BN) is visible to every valid row of the work-group: it lies
+// in the context prefix [0, ctx), or its part past the prefix lies inside every
+// valid row's band.  (A work-group with no valid row has full_lo > full_hi.)
+HSTU_HD bool block_tile_full(const BlockBand &bb, int32_t ctx, int32_t j0, int32_t BN) {
+    const int32_t j1 = j0 + BN;
+    return j1 <= ctx || (bb.full_lo <= imax(j0, ctx) && j1 - 1 <= bb.full_hi);
+}
+
 // Key tiles a q-tile needs: the context tiles [0, ceil(ctx/BN)) and the band
 // tiles covering [band_lo, band_hi] (the union of its rows' bands), merged when
 // they touch, then intersected with the split's tile range [t_begin, t_end).

@@ -1,0 +1,204 @@
+// plan_check.cpp - host build of the forward kernels' planner (hstu_plan.h),
+// checked against dense masks read from stdin.  Test infrastructure: built by
+// tests/test_plan_cpu.py with g++ under AddressSanitizer and
+// UndefinedBehaviorSanitizer; the masks come from an independent evaluation of
+// the mask rule (the rule form, row by row), never from this planner.
+//
+// Input, one case per two lines:
+//   S_q S_kv C T cross L M causal
+//   <S_q * S_kv characters '0' / '1': the dense mask, row-major>
+// For every case and every (BM, BN) of kTiles it checks:
+//   interval form   span_visible(row_span(i), j) == mask[i][j] for every (i, j);
+//   tile list       the key tiles make_tile_list keeps for a q-tile cover every
+//                   visible pair of its rows; a tile outside the list holds none;
+//                   the list is increasing and inside [0, ceil(S_kv / BN));
+//   row classes     tile_state EMPTY: no visible key of the row in the tile; FULL:
+//                   every key of the tile exists and is visible; rows past the
+//                   sequence are EMPTY;
+//   work-group test block_tile_full (the pipelined body's unmasked tiles): every
+//                   valid row of the q-tile sees every key of the tile;
+//   splits          split_range cuts [0, nt) into contiguous, disjoint ranges
+//                   that cover it (1 .. 6 splits and 16), and the per-split tile
+//                   lists concatenate to the unsplit list;
+//   pair count      counting as the device count kernel does (work-group test,
+//                   then row classes, then the predicate) gives the mask's
+//                   number of visible pairs.
+// Prints "checked <cases> cases, <tiles> tiles" and exits 0, or prints the first
+// failure and exits 1.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "hstu_plan.h"
+
+using namespace hstu;
+
+namespace {
+
+struct TileCfg {
+    int BM, BN;
+};
+// tiny tiles to exercise the tiling logic at sizes the sweep can enumerate, and
+// the kernels' own (128 query rows; 128, 64 or 32 keys for head dims 64, 128, 256)
+constexpr TileCfg kTiles[] = {{1, 1}, {2, 2}, {3, 2}, {4, 3}, {5, 8}, {8, 4}, {128, 128}, {128, 64}, {128, 32}};
+constexpr int kSplits[] = {1, 2, 3, 4, 5, 6, 16};
+
+long g_case = 0;
+long g_tiles = 0;
+
+[[noreturn]] void fail(const char *what, int a = -1, int b = -1, int c = -1) {
+    std::printf("FAIL case %ld: %s (%d, %d, %d)\n", g_case, what, a, b, c);
+    std::exit(1);
+}
+
+struct Case {
+    int S_q, S_kv, C, T, cross, L, M, causal;
+    std::vector<unsigned char> mask;  // [S_q][S_kv]
+    bool vis(int i, int j) const { return mask[(size_t)i * S_kv + j] != 0; }
+};
+
+SeqGeom geom(const Case &c, int32_t *off_q, int32_t *off_kv, int32_t *targets, KernelParams &p) {
+    std::memset(&p, 0, sizeof(p));
+    off_q[0] = 0;
+    off_q[1] = c.S_q;
+    off_kv[0] = 0;
+    off_kv[1] = c.S_kv;
+    targets[0] = c.T;
+    p.off_q = off_q;
+    p.off_kv = off_kv;
+    p.num_targets = targets;
+    p.B = 1;
+    p.H = 1;
+    p.jagged = 1;
+    p.cross = c.cross;
+    p.causal = c.causal;
+    p.G = 1;
+    p.per_group = 1;
+    p.groups[0].local_len = c.L;
+    p.groups[0].context_len = c.C;
+    p.groups[0].minfull_len = c.M;
+    p.groups[0].attn_scale = 1.0f;
+    return seq_geom(p, 0);
+}
+
+void check_case(const Case &c) {
+    int32_t off_q[2], off_kv[2], targets[1];
+    KernelParams p;
+    const SeqGeom s = geom(c, off_q, off_kv, targets, p);
+    if (s.S_q != c.S_q || s.S_kv != c.S_kv) fail("sequence lengths", s.S_q, s.S_kv);
+
+    // interval form against the rule form
+    long visible = 0;
+    for (int i = -2; i < c.S_q + 2; ++i) {
+        const RowSpan r = row_span(s, c.causal, i);
+        if ((i >= 0 && i < c.S_q) != r.valid) fail("row validity", i);
+        if (!r.valid) continue;
+        for (int j = 0; j < c.S_kv; ++j) {
+            if (span_visible(r, j) != c.vis(i, j)) fail("interval form differs from the mask", i, j);
+            visible += c.vis(i, j);
+        }
+    }
+
+    for (const TileCfg &tc : kTiles) {
+        const int BM = tc.BM, BN = tc.BN;
+        const int nt = (c.S_kv + BN - 1) / BN;
+        long counted = 0;
+        for (int r0 = 0; r0 < c.S_q; r0 += BM) {
+            BlockBand band = block_band_init();
+            std::vector<RowSpan> rows(BM);
+            for (int k = 0; k < BM; ++k) {
+                rows[k] = row_span(s, c.causal, r0 + k);
+                band = block_band_join(band, row_band(rows[k]));
+            }
+            const TileList tl = make_tile_list(s.Ck, true, band.lo, band.hi, BN, 0, nt);
+            std::vector<char> in_list(nt > 0 ? nt : 1, 0);
+            int prev = -1;
+            for (int n = 0; n < tl.count(); ++n) {
+                const int t = tl.at(n);
+                if (t <= prev || t < 0 || t >= nt) fail("tile list not increasing or out of range", r0, t, n);
+                prev = t;
+                in_list[t] = 1;
+            }
+            for (int t = 0; t < nt; ++t) {
+                const int j0 = t * BN, j1 = j0 + BN;
+                ++g_tiles;
+                const bool wg_full = block_tile_full(band, s.Ck, j0, BN);
+                if (wg_full && !in_list[t]) fail("work-group-full tile not in the list", r0, t);
+                for (int k = 0; k < BM; ++k) {
+                    const int i = r0 + k;
+                    const RowSpan &r = rows[k];
+                    int nvis = 0;
+                    if (r.valid)
+                        for (int j = j0; j < j1 && j < c.S_kv; ++j) nvis += c.vis(i, j);
+                    if (!in_list[t]) {
+                        if (nvis) fail("a skipped tile holds visible pairs", i, t);
+                        continue;
+                    }
+                    const int32_t st = tile_state(r, j0, j1);
+                    if (!r.valid && st != kTileEmpty) fail("row past the sequence not EMPTY", i, t);
+                    if (st == kTileEmpty && nvis) fail("EMPTY tile holds visible pairs", i, t);
+                    if (st == kTileFull && (j1 > c.S_kv || nvis != BN)) fail("FULL tile not all visible", i, t, nvis);
+                    if (wg_full && r.valid && (j1 > c.S_kv || nvis != BN))
+                        fail("work-group-full tile not all visible to a valid row", i, t, nvis);
+                    // the device count kernel's rule
+                    if (!r.valid) continue;
+                    if (wg_full || st == kTileFull) {
+                        counted += BN;
+                    } else if (st == kTilePartial) {
+                        for (int j = j0; j < j1; ++j) counted += span_visible(r, j) ? 1 : 0;
+                    }
+                }
+            }
+            // split-KV: contiguous ranges covering [0, nt); lists concatenate
+            for (int ns : kSplits) {
+                int expect_b = 0;
+                std::vector<int> cat;
+                for (int sp = 0; sp < ns; ++sp) {
+                    int32_t tb = -7, te = -7;
+                    split_range(c.S_kv, BN, ns, sp, &tb, &te);
+                    if (tb != expect_b || te < tb || te > nt) fail("split ranges do not partition the tiles", ns, sp, tb);
+                    expect_b = te;
+                    const TileList st = make_tile_list(s.Ck, true, band.lo, band.hi, BN, tb, te);
+                    for (int n = 0; n < st.count(); ++n) {
+                        const int t = st.at(n);
+                        if (t < tb || t >= te) fail("split list leaves its range", ns, sp, t);
+                        cat.push_back(t);
+                    }
+                }
+                if (expect_b != nt) fail("split ranges do not reach the last tile", ns, expect_b, nt);
+                if ((int)cat.size() != tl.count()) fail("split lists do not concatenate to the list", ns);
+                for (int n = 0; n < tl.count(); ++n)
+                    if (cat[n] != tl.at(n)) fail("split lists do not concatenate to the list", ns, n);
+            }
+        }
+        if (counted != visible) fail("pair count by tile classes differs from the mask's", BM, BN, (int)(counted - visible));
+    }
+}
+
+}  // namespace
+
+int main() {
+    Case c;
+    while (std::scanf("%d %d %d %d %d %d %d %d", &c.S_q, &c.S_kv, &c.C, &c.T, &c.cross, &c.L, &c.M, &c.causal) == 8) {
+        if (c.S_q < 0 || c.S_kv < 0 || c.S_q > 100000 || c.S_kv > 100000) fail("bad header");
+        c.mask.assign((size_t)c.S_q * c.S_kv, 0);
+        std::string line;
+        line.resize((size_t)c.S_q * c.S_kv + 1);
+        if (c.S_q * c.S_kv > 0) {
+            if (std::scanf("%s", &line[0]) != 1) fail("missing mask");
+            for (size_t k = 0; k < c.mask.size(); ++k) {
+                if (line[k] != '0' && line[k] != '1') fail("bad mask character", (int)k);
+                c.mask[k] = line[k] == '1';
+            }
+        } else {
+            char dash[8];
+            if (std::scanf("%7s", dash) != 1) fail("missing empty-mask marker");
+        }
+        check_case(c);
+        ++g_case;
+    }
+    std::printf("checked %ld cases, %ld tiles\n", g_case, g_tiles);
+    return 0;
+}

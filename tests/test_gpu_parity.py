@@ -296,3 +296,31 @@ def test_max_head_dim_and_ragged_tiles():
                 cross=False, causal=True, softmax=False, alpha=0.0, groups=groups,
                 uih_q=[1, 257, 300], targets=[31, 0, 7], seed=3)
     _check_full(w)
+
+
+@pytest.mark.parametrize("softmax,local_len,context_len", [(False, 0, 6), (False, 5, 6), (True, 0, 6),
+                                                           (True, 7, 0)])
+def test_self_equals_cross_on_context_and_history_prefix(softmax, local_len, context_len):
+    """Target keys are never attended (CK README "Masking": targets excluded from
+    attention), so self-attention equals cross-attention whose keys and values are
+    each sequence's [context | UIH] prefix, with the queries unchanged (the query
+    history is then the whole key history: bottom-right alignment is the identity).
+    The same key tiles in the same order: bit for bit."""
+    groups = [W.MaskGroup(local_len, context_len, 4 if local_len else 0, 0.0)]
+    kw = dict(dtype="bf16", batch=4, nhead=2, hdim_qk=128, hdim_v=128, jagged=True, causal=True,
+              softmax=softmax, alpha=0.0, groups=groups)
+    uih, tg = [300, 0, 129, 77], [5, 3, 0, 31]
+    ws = W.build("self", cross=False, uih_q=uih, targets=tg, seed=61, **kw)
+    wc = W.build("cross", cross=True, uih_q=uih, targets=tg, uih_kv=uih, materialize=False, **kw)
+    keep = np.concatenate([np.arange(ws.q_offsets[b], ws.q_offsets[b] + context_len + uih[b])
+                           for b in range(ws.batch)]).astype(np.int64)
+    wc.q_bits = ws.q_bits
+    wc.k_bits, wc.v_bits = ws.k_bits[keep], ws.v_bits[keep]
+    assert len(keep) == wc.kv_offsets[-1]
+    a = DeviceInputs(ws).forward()
+    b = DeviceInputs(wc).forward()
+    torch.cuda.synchronize()
+    if softmax:
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    else:
+        assert torch.equal(a, b)
