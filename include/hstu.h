@@ -60,6 +60,7 @@ extern "C" {
 #define HSTU_MAX_SPLITS 128
 #define HSTU_RAB_TIME_BUCKETS 11 /* time-gap buckets of the relative attention bias */
 #define HSTU_RAB_MAX_POS 2048    /* longest positional bias table */
+#define HSTU_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20) /* static scratch of hstu_fwd_splitkv_noalloc */
 
 typedef enum {
     HSTU_OK = 0,
@@ -159,6 +160,21 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
  * 2; schedule 3 needs it). */
 hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, void *ws,
                                size_t ws_bytes, void *hip_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it):
+ * hstu_fwd_splitkv (num_splits == 1: hstu_fwd) with its workspace - the split-KV
+ * partial results and the persistent schedule's work queues - in a static device
+ * array of HSTU_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends.  The caller passes inputs and outputs as for
+ * hstu_fwd_splitkv; the call allocates and frees nothing.  A problem whose
+ * workspace (hstu_fwd_workspace_size) exceeds the scratch is rejected with
+ * HSTU_ERR_WORKSPACE before anything runs.  All calls on one GPU share its
+ * scratch (each call's kernels overwrite what they use; nothing needs to start at
+ * zero): calls that overlap in time on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.  The first call on a device looks
+ * the scratch's address up (hipGetSymbolAddress) with that device current. */
+hstu_status_t hstu_fwd_splitkv_noalloc(const hstu_fwd_args_t *args, int32_t num_splits, void *hip_stream);
 
 /* Counts, on the device, the visible (b, h, i, j) pairs inside the key tiles the
  * forward kernel schedules, with the kernel's own mask predicate.  Equal to the

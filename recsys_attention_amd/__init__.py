@@ -26,7 +26,8 @@ import torch
 
 from . import _abi
 
-__all__ = ["HstuGroup", "hstu_fwd", "hstu_fwd_splitkv", "hstu_count_visible_pairs",
+__all__ = ["HstuGroup", "hstu_fwd", "hstu_fwd_splitkv", "hstu_fwd_splitkv_noalloc",
+           "hstu_count_visible_pairs",
            "workspace_size", "group_max_uih", "is_available", "library_path",
            "hstu_linear", "hstu_norm_gate", "hstu_layer", "hstu_layer_workspace_size"]
 
@@ -99,7 +100,7 @@ class _Call:
 
     def __init__(self, q, k, v, *, seq_offsets, seq_offsets_kv, num_targets, max_seqlen_q,
                  max_seqlen_kv, cross, causal, softmax, alpha, groups, return_lse, out, schedule,
-                 rab_timestamps=None, rab_time=None, rab_pos=None):
+                 rab_timestamps=None, rab_time=None, rab_pos=None, lse_out=None):
         for t, n in ((q, "q"), (k, "k"), (v, "v")):
             if not t.is_cuda:
                 raise ValueError(f"{n} must be a device tensor")
@@ -145,7 +146,12 @@ class _Call:
         if return_lse:
             if not softmax:
                 raise ValueError("return_lse is for the softmax variant")
-            self.lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+            if lse_out is None:
+                lse_out = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+            if (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != tuple(lse_shape)
+                    or not lse_out.is_contiguous()):
+                raise ValueError(f"lse_out must be a contiguous float32 tensor {list(lse_shape)}")
+            self.lse = lse_out
         self.out = out
         self.groups = _groups_c(groups)
         _check_rab(rab_timestamps, rab_time, rab_pos, H, total_q)
@@ -271,6 +277,24 @@ def hstu_fwd_splitkv(q, k, v, num_splits, *, workspace=None, stream=None, **kw):
         ws_ptr, ws_bytes = _workspace(lib, c, num_splits, workspace, q.device)
         _abi.check(lib.hstu_fwd_splitkv(ctypes.byref(c.args), int(num_splits), ws_ptr, ws_bytes,
                                         c.stream(stream)))
+    return _result(c, d["return_lse"])
+
+
+def hstu_fwd_splitkv_noalloc(q, k, v, num_splits, *, out, lse_out=None, stream=None, **kw):
+    """hstu_fwd_splitkv for callers that cannot allocate: the split-KV partials and
+    the work queues go to the library's static scratch (HSTU_NOALLOC_SCRATCH_BYTES
+    per GPU), and the caller passes the output (and, with return_lse, lse_out):
+    nothing is allocated.  Calls that overlap in time on one GPU race (they share
+    its scratch)."""
+    lib = _abi.load()
+    if out is None:
+        raise ValueError("the allocation-free call needs out")
+    d = _call_kw(kw)
+    if d["return_lse"] and lse_out is None:
+        raise ValueError("the allocation-free call needs lse_out with return_lse")
+    d.update(out=out)
+    c = _Call(q, k, v, lse_out=lse_out, **d)
+    _abi.check(lib.hstu_fwd_splitkv_noalloc(ctypes.byref(c.args), int(num_splits), c.stream(stream)))
     return _result(c, d["return_lse"])
 
 

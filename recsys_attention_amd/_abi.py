@@ -23,13 +23,14 @@ HSTU_MAX_SPLITS = 128
 HSTU_ABI_VERSION = 3
 HSTU_RAB_TIME_BUCKETS = 11
 HSTU_RAB_MAX_POS = 2048
+HSTU_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 HSTU_ACT_NONE = 0
 HSTU_ACT_SILU = 1
 
 # every symbol include/*.h declares
 EXPORTED = ("hstu_validate_args", "hstu_fwd_workspace_size", "hstu_fwd", "hstu_fwd_splitkv",
-            "hstu_count_visible_pairs", "hstu_status_string", "hstu_last_error",
+            "hstu_fwd_splitkv_noalloc", "hstu_count_visible_pairs", "hstu_status_string", "hstu_last_error",
             "hstu_abi_version",
             "hstu_linear_fwd", "hstu_norm_gate_fwd", "hstu_layer_workspace_size", "hstu_layer_fwd")
 
@@ -105,6 +106,8 @@ def load(path: str = LIB_PATH):
     lib.hstu_fwd_splitkv.argtypes = [P, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
     lib.hstu_fwd_splitkv.restype = ctypes.c_int
+    lib.hstu_fwd_splitkv_noalloc.argtypes = [P, ctypes.c_int32, ctypes.c_void_p]
+    lib.hstu_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.hstu_count_visible_pairs.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
     lib.hstu_count_visible_pairs.restype = ctypes.c_int
     lib.hstu_status_string.argtypes = [ctypes.c_int]

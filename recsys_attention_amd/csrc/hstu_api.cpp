@@ -298,6 +298,23 @@ hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, 
                       "combine kernel launch");
 }
 
+hstu_status_t hstu_fwd_splitkv_noalloc(const hstu_fwd_args_t *args, int32_t num_splits, void *hip_stream) {
+    hstu_status_t st = validate(args);
+    if (st != HSTU_OK) return st;
+    if (num_splits < 1 || num_splits > HSTU_MAX_SPLITS)
+        return fail(HSTU_ERR_INVALID_ARG, "num_splits %d not in 1..%d", num_splits, HSTU_MAX_SPLITS);
+    const size_t need = workspace_bytes(args, num_splits);
+    if (need > hstu::kScratchBytes)
+        return fail(HSTU_ERR_WORKSPACE,
+                    "this problem needs %zu bytes of workspace; the static scratch holds %zu (use hstu_fwd_splitkv "
+                    "with a workspace of hstu_fwd_workspace_size bytes)",
+                    need, hstu::kScratchBytes);
+    if (rows_q(args) == 0 || args->batch == 0) return HSTU_OK;
+    void *ws = nullptr;
+    if ((st = hip_status(hstu::scratch_region(&ws), "static scratch address")) != HSTU_OK) return st;
+    return hstu_fwd_splitkv(args, num_splits, ws, hstu::kScratchBytes, hip_stream);
+}
+
 hstu_status_t hstu_count_visible_pairs(const hstu_fwd_args_t *args, unsigned long long *d_count,
                                        void *hip_stream) {
     hstu_status_t st = validate(args);

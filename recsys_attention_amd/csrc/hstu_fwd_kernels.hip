@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "hstu_launch.h"
@@ -1295,6 +1296,34 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(KernelParams p)
 }
 
 // ------------------------------------------------------------------ launchers
+
+// Static scratch of the allocation-free entry point: split-KV partials and the
+// persistent schedule's work queues of one call, in a file-scope device array
+// that every GPU the library runs on holds (at its own address) until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in): the address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_region(void **ptr) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 
 // compute units of the current device (cached per device)
 static int current_device_cus() {

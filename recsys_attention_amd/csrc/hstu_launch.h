@@ -21,4 +21,11 @@ hipError_t launch_forward(const KernelParams &p, int dtype, int D, int DV, bool 
 hipError_t launch_combine(const KernelParams &p, int dtype, int D, bool softmax, hipStream_t stream);
 hipError_t launch_count(const KernelParams &p, int D, unsigned long long *count, hipStream_t stream);
 
+// The allocation-free entry point's static scratch (HSTU_NOALLOC_SCRATCH_BYTES,
+// 256-byte aligned): its device address on the current device, looked up on the
+// first call per device.  Calls on one device share it.
+constexpr size_t kScratchBytes = HSTU_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_region(void **ptr);
+
 }  // namespace hstu

@@ -303,3 +303,16 @@ def test_layer_with_no_tokens_is_a_no_op(lib):
     attn = _args(batch=0, total_q=0, seq_offsets_q=None, num_targets=None)
     a = _layer(attn)
     assert lib.hstu_layer_fwd(ctypes.byref(a), None, 0, None) == _abi.HSTU_OK
+
+
+def test_noalloc_rejects_beyond_the_static_scratch(lib):
+    """The allocation-free entry point refuses, before any HIP call, a problem whose
+    workspace exceeds its static scratch (here 128 splits of 8038 rows x 4 heads x
+    128 fp32 partial columns)."""
+    a = _args()
+    need = lib.hstu_fwd_workspace_size(ctypes.byref(a), 128)
+    assert need > _abi.HSTU_NOALLOC_SCRATCH_BYTES
+    assert lib.hstu_fwd_splitkv_noalloc(ctypes.byref(a), 128, None) == _abi.HSTU_ERR_WORKSPACE
+    assert b"static scratch" in lib.hstu_last_error()
+    assert lib.hstu_fwd_splitkv_noalloc(ctypes.byref(a), 0, None) == _abi.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_fwd_splitkv_noalloc(ctypes.byref(_args(dtype=9)), 1, None) == _abi.HSTU_ERR_INVALID_ARG
