@@ -175,14 +175,26 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 // SiLU on one 32-key block of raw scores x = q.k, in place, without the factor
 // alpha: p = x / (1 + 2^(-alpha log2e x)) = SiLU(alpha x) / alpha; zeroed
 // outside the row's visible keys when MASK.
+//
+// With MASK, the row's visibility of the block's 16 keys comes as one bit mask
+// (lane_key_mask: bit i for key key0 + 8 (i / 4) + i % 4), and each score is
+// ANDed with its bit spread over the word (v_bfe_i32: 0 or all ones): two VALU
+// instructions per score instead of evaluating the interval test per key.
 template <bool MASK>
 __device__ __forceinline__ void silu_block(f32x16_t &x, float neg_alpha_log2e, const RowSpan &span,
                                            int key0) {
+    const uint32_t vis = MASK ? lane_key_mask(span, key0) : 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float v = x[i];
         float pv = v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * neg_alpha_log2e));
-        if constexpr (MASK) pv = span_visible(span, key0 + 8 * (i >> 2) + (i & 3)) ? pv : 0.0f;
+        if constexpr (MASK) {
+            // written out so the compiler keeps the two instructions (it otherwise
+            // turns the select into a compare and a select)
+            int32_t keep;
+            asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(vis), "n"(i));
+            pv = __builtin_bit_cast(float, __builtin_bit_cast(int32_t, pv) & keep);
+        }
         x[i] = pv;
     }
 }
@@ -945,22 +957,49 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             scale = l > 0.f ? s.attn_scale / l : 0.f;
             lse_val = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
         }
-        if (!span.valid) return;
+        // (a lane whose row lies past the sequence still takes part in the
+        // staged store below; only its row is not written)
+        if (SPLIT && !span.valid) return;
         const int64_t grow = s.q0 + bp.row;  // token row of o
         if constexpr (!SPLIT) {
-            uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * DV + 4 * g;
+            // The wave's 32 output rows go through LDS (both ring stages are free
+            // once the last tile's barrier has passed; each wave uses a region of
+            // its own, so no barrier is needed here) and leave as whole rows: a
+            // lane holds 8-byte pieces of its row, scattered over 16-byte chunks;
+            // read back, each lane stores one 16-byte chunk and the wave writes
+            // LPR-lane runs of complete rows (8 stores for hdim 128 instead of 16
+            // stores of 32 scattered 16-byte pieces).  Rows of CH 16-byte chunks
+            // sit at a pitch of LPR chunks (a power of two), chunk c of row r at
+            // c ^ (r & SWZ) against bank conflicts.
+            constexpr int CH = DV / 8;
+            constexpr int LPR = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
+            constexpr int SWZ = (LPR < 16 ? LPR : 16) - 1;
+            constexpr int PITCH = LPR * 16;
+            static_assert(NW * 32 * PITCH <= 2 * C::STAGE, "the output staging fits in the ring");
+            uint8_t *stg = &lds[0][0] + wave * 32 * PITCH;
 #pragma unroll
             for (int nb = 0; nb < C::NDB; ++nb) {
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const f32x16_t &a = oacc[nb];
-                    *(u32x2_t *)(op + nb * 32 + 8 * i4) =
+                    const int c = 4 * nb + i4;
+                    *(u32x2_t *)(stg + r32 * PITCH + ((c ^ (r32 & SWZ)) * 16) + 8 * g) =
                         u32x2_t{E::pack2(a[4 * i4] * scale, a[4 * i4 + 1] * scale),
                                 E::pack2(a[4 * i4 + 2] * scale, a[4 * i4 + 3] * scale)};
                 }
             }
+            constexpr int RPI = 64 / LPR;  // rows per store instruction
+            const int c = lane % LPR;
+            const int64_t wtok = s.q0 + (int64_t)wrow0;  // token of the wave's first row
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int r = k * RPI + lane / LPR;
+                const u32x4_t v = *(const u32x4_t *)(stg + r * PITCH + ((c ^ (r & SWZ)) * 16));
+                if (c < CH && wrow0 + r < s.S_q)
+                    *(u32x4_t *)((uint16_t *)p.o + (wtok + r) * p.o_stride + h * DV + c * 8) = v;
+            }
             if constexpr (SOFTMAX) {
-                if (p.lse != nullptr && g == 0) {
+                if (p.lse != nullptr && g == 0 && span.valid) {
                     const int64_t li = p.jagged ? (int64_t)h * p.total_rows + grow
                                                 : ((int64_t)bp.it.b * p.H + h) * p.seqlen_q + bp.row;
                     p.lse[li] = lse_val;

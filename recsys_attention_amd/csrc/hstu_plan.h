@@ -161,6 +161,23 @@ HSTU_HD bool block_tile_full(const BlockBand &bb, int32_t ctx, int32_t j0, int32
     return j1 <= ctx || (bb.full_lo <= imax(j0, ctx) && j1 - 1 <= bb.full_hi);
 }
 
+// The 32 keys one lane scores in a 64-key tile: element e (0..31) is key
+// jb + 8 (e / 4) + e % 4 (four consecutive keys of every eight).  Bit e of
+// lane_key_mask is set when the row sees that key.  The element offsets grow
+// with e, so the keys below u are the first cnt(u) = 4 (u / 8) + min(u % 8, 4)
+// elements (u clamped to 0..64): each of the row's two intervals is a run of
+// consecutive bits.
+HSTU_HD uint32_t lane_prefix_bits(int32_t u) {
+    u = imin(imax(u, 0), 64);
+    const int32_t n = 4 * (u >> 3) + imin(u & 7, 4);  // 0..32
+    return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+}
+HSTU_HD uint32_t lane_key_mask(const RowSpan &r, int32_t jb) {
+    const uint32_t ctx = lane_prefix_bits(r.ctx - jb);
+    if (r.lo > r.hi) return ctx;
+    return ctx | (lane_prefix_bits(r.hi + 1 - jb) & ~lane_prefix_bits(r.lo - jb));
+}
+
 // Key tiles a q-tile needs: the context tiles [0, ceil(ctx/BN)) and the band
 // tiles covering [band_lo, band_hi] (the union of its rows' bands), merged when
 // they touch, then intersected with the split's tile range [t_begin, t_end).

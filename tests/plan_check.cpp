@@ -17,6 +17,9 @@
 //                   sequence are EMPTY;
 //   work-group test block_tile_full (the pipelined body's unmasked tiles): every
 //                   valid row of the q-tile sees every key of the tile;
+//   lane masks      lane_key_mask (the pipelined body's masked tiles): bit e is
+//                   set exactly when the row sees key jb + 8 (e / 4) + e % 4, for
+//                   64-key tiles and both lane groups' first keys;
 //   splits          split_range cuts [0, nt) into contiguous, disjoint ranges
 //                   that cover it (1 .. 6 splits and 16), and the per-split tile
 //                   lists concatenate to the unsplit list;
@@ -142,6 +145,17 @@ void check_case(const Case &c) {
                     if (st == kTileFull && (j1 > c.S_kv || nvis != BN)) fail("FULL tile not all visible", i, t, nvis);
                     if (wg_full && r.valid && (j1 > c.S_kv || nvis != BN))
                         fail("work-group-full tile not all visible to a valid row", i, t, nvis);
+                    // the pipelined body's per-lane key masks (64-key tiles: lanes start
+                    // at j0 and j0 + 4)
+                    if (BN == 64)
+                        for (int jb = j0; jb <= j0 + 4; jb += 4) {
+                            const uint32_t m = lane_key_mask(r, jb);
+                            for (int e = 0; e < 32; ++e) {
+                                const int j = jb + 8 * (e / 4) + e % 4;
+                                const bool v = r.valid && j < c.S_kv && c.vis(i, j);
+                                if (((m >> e) & 1u) != (v ? 1u : 0u)) fail("lane key mask differs from the mask", i, j, jb);
+                            }
+                        }
                     // the device count kernel's rule
                     if (!r.valid) continue;
                     if (wg_full || st == kTileFull) {
