@@ -19,6 +19,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the work queues' atomics are single-lane already: the wave-aggregating
+    # rewrite of atomics only adds a wait for the result right after each one
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I" + os.path.join(_ROOT, "include"),
 ]
 

@@ -287,6 +287,7 @@ __device__ __forceinline__ void wait_all_loads_here() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
+
 #pragma clang diagnostic pop
 
 // Relative attention bias (HSTU explainer, "The relative attention bias").
@@ -782,6 +783,10 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         if (ntiles > 0) issue_loads(bp.tiles.at(0), 0);
         wait_all_loads();
         __syncthreads();
+        // key tile of step n's loads: tile n + 1, or, after the last tile, a tile
+        // past the sequence's end (the buffer range turns those loads into zeros
+        // without memory traffic, so no load needs a branch)
+        auto tile_ahead = [&](int n) { return n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN; };
 
         // Runs step(n, stage) on tiles n, n + 1, ... while more(n) holds.  Tile n
         // uses ring stage n & 1, passed as a template constant: each step body
@@ -797,23 +802,26 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 ++n;
             }
         };
+        // the end of a step: the next tile's loads have landed and every wave is
+        // done with this tile's stage
+        auto end_step = [&]() {
+            wait_all_loads_here();
+            __syncthreads();
+        };
 
         // one key tile through the generic body (any mask, any variant)
         auto generic_step = [&](int n, auto stage_const) {
             constexpr int buf = decltype(stage_const)::value;
+            constexpr int nbuf = buf ^ 1;
             if (n == ntiles - 2) reserve_next();
             if (n == ntiles - 1) fetch_next();
-            const bool has_next = n + 1 < ntiles;
-            // after the last tile the loads fall past the sequence's buffer range: they
-            // return zeros into the free stage without touching memory, so no load
-            // needs a branch
-            const int t_next = has_next ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
+            const int t_next = tile_ahead(n);
             const int j0 = bp.tiles.at(n) * BN;
             const int32_t st = tile_state(span, j0, j0 + BN);
             const bool wave_any = __ballot(st != kTileEmpty) != 0;
             const bool wave_mask = __ballot(span.valid && st != kTileFull) != 0;
 
-            issue_loads(t_next, buf ^ 1);
+            issue_loads(t_next, nbuf);
             if (wave_any) {
                 const uint8_t *stage = lds0 + buf * C::STAGE;
                 // scores and non-linearity at wave priority 1, P.V at 0 (as in the
@@ -909,41 +917,65 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                 }
             }
 
-            wait_all_loads_here();
-            __syncthreads();
+            end_step();
         };
         if constexpr (!SOFTMAX && D == 128 && DV == 128) {
-            // Tiles visible to every valid row of the work-group run through the
-            // software-pipelined body, in a loop of their own; the others through the
-            // generic body.  (Choosing between the two bodies per tile inside one loop
-            // made the compiler copy the 64 output accumulators between two register
-            // sets on every tile.)
-            auto full_step = [&](int n, auto stage_const) {
+            // Every key tile runs through the software-pipelined body.  In a tile
+            // that some valid row of the work-group sees only in part, the mask
+            // enters the score MFMAs' initial accumulator: a hidden score starts at
+            // mask_val = 1e30 with the sign of -alpha, so that -alpha log2e times it
+            // is huge and positive, exp2 of it +inf, and SiLU of it exactly zero
+            // (with the bias, a visible score keeps its bias and a hidden one is
+            // replaced).  Building the accumulators costs two VALU instructions per
+            // score (v_bfe_i32 of the lane's key bit, then a bitfield select), only
+            // in those tiles; one body, one call site, so the loop keeps one
+            // register set.  A wave none of whose rows sees such a tile only issues
+            // its share of the next tile's loads.
+            const float mask_val = copysignf(1e30f, neg_alpha_log2e);
+            auto step = [&](int n, auto stage_const) {
                 constexpr int buf = decltype(stage_const)::value;
+                constexpr int nbuf = buf ^ 1;
                 if (n == ntiles - 2) reserve_next();
                 if (n == ntiles - 1) fetch_next();
-                const int t_next = n + 1 < ntiles ? bp.tiles.at(n + 1) : (s.S_kv + 2 * BN - 1) / BN;
+                const int t_next = tile_ahead(n);
+                const int j0 = bp.tiles.at(n) * BN;
                 f32x16_t init[2] = {};
                 if constexpr (RAB) {
-                    rab_tile<2, BN>(init, rab_inv_alpha, bp.row, bp.tiles.at(n) * BN, g, wrow0, pos_lds,
-                                    rab_pos_len, ts_lds[buf], t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos,
-                                    has_time, lane);
-                    issue_ts(t_next, buf ^ 1);
+                    rab_tile<2, BN>(init, rab_inv_alpha, bp.row, j0, g, wrow0, pos_lds, rab_pos_len, ts_lds[buf],
+                                    t_row, bp.row < s.S_q, s.S_kv, oct_lds, has_pos, has_time, lane);
+                    issue_ts(t_next, nbuf);
                 }
-                silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
-                                          init[0], init[1], [&](int idx) {
-                                              if (idx < LPT) issue_one(t_next, buf ^ 1, idx);
-                                          });
-                wait_all_loads_here();
-                __syncthreads();
+                bool wave_any = true;
+                if (!bp.tile_full(j0, BN)) {
+                    wave_any = __ballot(tile_state(span, j0, j0 + BN) != kTileEmpty) != 0;
+                    const uint32_t vis = lane_key_mask(span, j0 + 4 * g);
+                    const uint32_t mv = __builtin_bit_cast(uint32_t, mask_val);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            int32_t keep;  // bit 16 kb + i of vis spread over the word
+                            asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(vis), "n"(16 * kb + i));
+                            // (through a scalar copy: __builtin_bit_cast of a vector element
+                            // read the vector's first element here)
+                            const float cur = init[kb][i];
+                            const uint32_t ib = __float_as_uint(cur);
+                            init[kb][i] = __uint_as_float((ib & (uint32_t)keep) | (mv & ~(uint32_t)keep));
+                        }
+                }
+                if (wave_any) {
+                    silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
+                                              init[0], init[1], [&](int idx) {
+                                                  if (idx < LPT) issue_one(t_next, nbuf, idx);
+                                              });
+                } else {
+#pragma unroll
+                    for (int idx = 0; idx < LPT; ++idx) issue_one(t_next, nbuf, idx);
+                }
+                end_step();
             };
-            auto full = [&](int n) { return n < ntiles && bp.tile_full(bp.tiles.at(n) * BN, BN); };
-            auto mixed = [&](int n) { return n < ntiles && !bp.tile_full(bp.tiles.at(n) * BN, BN); };
             int n = 0;
-            while (n < ntiles) {
-                run_tiles(n, mixed, generic_step);
-                run_tiles(n, full, full_step);
-            }
+            run_tiles(n, [&](int n) { return n < ntiles; }, step);
         } else {
             int n = 0;
             run_tiles(n, [&](int n) { return n < ntiles; }, generic_step);

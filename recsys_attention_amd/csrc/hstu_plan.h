@@ -44,23 +44,34 @@ HSTU_HD SeqGeom seq_geom(const KernelParams &p, int32_t b) {
     SeqGeom s;
     s.group = b / p.per_group;
     const GroupDev &g = p.groups[s.group];
+    // every load of the sequence's metadata is issued before any of the values
+    // is used, so that on the device they cost one memory round trip, not three
+    int32_t q_lo = 0, q_hi = 0, kv_lo = 0, kv_hi = 0, T = 0;
     if (p.jagged) {
-        s.q0 = p.off_q[b];
-        s.S_q = (int32_t)(p.off_q[b + 1] - p.off_q[b]);
-        if (p.cross) {
-            s.kv0 = p.off_kv[b];
-            s.S_kv = (int32_t)(p.off_kv[b + 1] - p.off_kv[b]);
-        } else {
-            s.kv0 = s.q0;
-            s.S_kv = s.S_q;
-        }
+        // (without targets the count is read from the offsets and discarded)
+        const int32_t *ko = p.cross ? p.off_kv : p.off_q;
+        const int32_t *tp = p.num_targets ? p.num_targets : p.off_q;
+        q_lo = p.off_q[b];
+        q_hi = p.off_q[b + 1];
+        kv_lo = ko[b];
+        kv_hi = ko[b + 1];
+        const int32_t t_raw = tp[b];
+        T = p.num_targets ? t_raw : 0;
+    } else if (p.num_targets) {
+        T = p.num_targets[b];
+    }
+    if (p.jagged) {
+        s.q0 = q_lo;
+        s.S_q = q_hi - q_lo;
+        s.kv0 = kv_lo;
+        s.S_kv = kv_hi - kv_lo;
     } else {
         s.q0 = (int64_t)b * p.seqlen_q;
         s.kv0 = (int64_t)b * p.seqlen_kv;
         s.S_q = p.seqlen_q;
         s.S_kv = p.seqlen_kv;
     }
-    const int32_t T = p.num_targets ? imax(p.num_targets[b], 0) : 0;
+    T = imax(T, 0);
     s.Cq = imin(g.context_len, s.S_q);
     const int32_t Tq = imin(T, s.S_q - s.Cq);
     s.Uq = s.S_q - s.Cq - Tq;
