@@ -185,11 +185,39 @@ size_t queue_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     fill_params(a, num_splits, p);
     return hstu::queue_bytes(p);
 }
-size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+constexpr int64_t kPersistentItems = 2048;
+
+// Heavy q-tiles.  When the per-item grid of an unsplit call (schedule left to
+// the library) holds fewer work-groups than the chip runs at once, the kernel's
+// time is that of its heaviest q-tile; the q-tiles with more than a chunk of key
+// tiles (heavy_chunk_tiles) are then cut into chunks that run side by side, and
+// a combine pass adds the chunks' partials up.  The workspace holds the partials
+// (kHeavyMaxSplits per q-tile) and each q-tile's record, after the rest.
+constexpr size_t kHeavyMaxBytes = (size_t)512 << 20;
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+size_t base_workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     return partial_bytes(a, num_splits) + (wants_queue(a) ? queue_bytes(a, num_splits) : 0);
 }
-
-constexpr int64_t kPersistentItems = 2048;
+size_t heavy_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+    if (a->schedule != 0 || num_splits != 1) return 0;
+    hstu::KernelParams p;
+    fill_params(a, 1, p);
+    const int64_t items = hstu::grid_size(p);
+    if (items >= kPersistentItems || items >= (int64_t)hstu::kChipCUs * hstu::groups_per_cu_for(a->hdim_qk))
+        return 0;
+    const int32_t bn = hstu::key_tile_for(a->hdim_qk);
+    if ((p.seqlen_kv + bn - 1) / bn <= hstu::heavy_chunk_tiles(bn)) return 0;  // no q-tile is cut
+    const size_t qtiles = (size_t)items;
+    const size_t rows = qtiles * hstu::kHeavyMaxSplits * (size_t)hstu::block_m_for(a->hdim_qk);
+    const size_t b = align256(rows * (size_t)a->hdim_v * sizeof(float)) +
+                     (a->softmax ? align256(rows * sizeof(float)) : 0) + align256(qtiles * 2 * sizeof(int32_t));
+    return b <= kHeavyMaxBytes ? b : 0;
+}
+size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+    const size_t base = base_workspace_bytes(a, num_splits);
+    const size_t heavy = heavy_bytes(a, num_splits);
+    return heavy ? align256(base) + heavy : base;
+}
 
 // Schedule and work queues of one call: the persistent schedule (3) when it is
 // asked for, or when the schedule is left to the library (0), the workspace
@@ -264,9 +292,30 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
     if ((st = check_grid(p)) != HSTU_OK) return st;
     if ((st = pick_schedule(args, 1, ws, ws_bytes, p)) != HSTU_OK) return st;
     if (p.total_rows == 0 || p.B == 0) return HSTU_OK;
-    return hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, false,
-                                           (hipStream_t)hip_stream),
-                      "forward kernel launch");
+    // heavy q-tiles cut into chunks when the per-item grid runs and the workspace
+    // holds the chunks' partials (hstu_fwd_workspace_size counts them)
+    const size_t heavy = heavy_bytes(args, 1);
+    if (heavy && p.queue == nullptr && ws != nullptr && aligned16(ws) && ws_bytes >= workspace_bytes(args, 1)) {
+        char *h = (char *)ws + align256(base_workspace_bytes(args, 1));
+        const size_t qtiles = (size_t)p.bh_pad * (size_t)p.num_qt;
+        const size_t rows = qtiles * hstu::kHeavyMaxSplits * (size_t)hstu::block_m_for(args->hdim_qk);
+        p.heavy = 1;
+        p.num_splits = hstu::kHeavyMaxSplits;
+        p.hpart_o = (float *)h;
+        h += align256(rows * (size_t)args->hdim_v * sizeof(float));
+        if (args->softmax) {
+            p.hpart_lse = (float *)h;
+            h += align256(rows * sizeof(float));
+        }
+        p.hmeta = (int32_t *)h;
+        if ((st = check_grid(p)) != HSTU_OK) return st;
+    }
+    hipStream_t stream = (hipStream_t)hip_stream;
+    st = hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, false, stream),
+                    "forward kernel launch");
+    if (st != HSTU_OK || !p.heavy) return st;
+    return hip_status(hstu::launch_heavy_combine(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, stream),
+                      "heavy q-tile combine launch");
 }
 
 hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, void *ws,
@@ -303,7 +352,9 @@ hstu_status_t hstu_fwd_splitkv_noalloc(const hstu_fwd_args_t *args, int32_t num_
     if (st != HSTU_OK) return st;
     if (num_splits < 1 || num_splits > HSTU_MAX_SPLITS)
         return fail(HSTU_ERR_INVALID_ARG, "num_splits %d not in 1..%d", num_splits, HSTU_MAX_SPLITS);
-    const size_t need = workspace_bytes(args, num_splits);
+    // (the heavy q-tiles' partials are left out: without room for them the
+    // q-tiles are not cut)
+    const size_t need = base_workspace_bytes(args, num_splits);
     if (need > hstu::kScratchBytes)
         return fail(HSTU_ERR_WORKSPACE,
                     "this problem needs %zu bytes of workspace; the static scratch holds %zu (use hstu_fwd_splitkv "

@@ -102,17 +102,6 @@ struct Tile {
     static_assert(LOADS * NT == BN * CPR && LOADS_V * NT == BN * CPRV, "the loads cover the tiles exactly");
 };
 
-__device__ __forceinline__ int32_t wave_min(int32_t x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = imin(x, __shfl_xor(x, o));
-    return x;
-}
-__device__ __forceinline__ int32_t wave_max(int32_t x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = imax(x, __shfl_xor(x, o));
-    return x;
-}
-
 // Per-work-group set-up shared by the attention and the pair-count kernels:
 // the work item, its sequence, the lane's row interval and the key-tile list.
 struct BlockPlan {
@@ -130,7 +119,7 @@ struct BlockPlan {
 
 template <int BN, int NW>
 __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, BlockPlan &bp,
-                                           int32_t *red, const WorkItem &item) {
+                                           const WorkItem &item) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     bp.it = item;
     if (!bp.it.valid) return false;
@@ -139,21 +128,9 @@ __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, Bl
     if (r0 >= bp.s.S_q) return false;
     bp.row = r0 + wave * 32 + (lane & 31);
     bp.span = row_span(bp.s, p.causal, bp.row);
-    // the work-group's BlockBand: each row's terms (row_band) reduced over the
-    // wave, then over the waves
-    const BlockBand mine = row_band(bp.span);
-    const BlockBand wb{wave_min(mine.lo), wave_max(mine.hi), wave_max(mine.full_lo), wave_min(mine.full_hi)};
-    if (lane == 0) {
-        red[4 * wave] = wb.lo;
-        red[4 * wave + 1] = wb.hi;
-        red[4 * wave + 2] = wb.full_lo;
-        red[4 * wave + 3] = wb.full_hi;
-    }
-    __syncthreads();
-    BlockBand band = block_band_init();
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-        band = block_band_join(band, BlockBand{red[4 * w], red[4 * w + 1], red[4 * w + 2], red[4 * w + 3]});
+    // the work-group's BlockBand in closed form from a few of its rows (uniform
+    // across the work-group: no reduction over the lanes, no barrier)
+    const BlockBand band = qtile_band(bp.s, p.causal, r0, r0 + 32 * NW - 1);
     bp.band = band;
     int32_t tb = 0, te = (bp.s.S_kv + BN - 1) / BN;
     if (split) split_range(bp.s.S_kv, BN, p.num_splits, bp.it.sp, &tb, &te);
@@ -579,7 +556,6 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     using E = Elem<DT>;
     // two stages of [K tile | V tile]
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][C::STAGE];
-    __shared__ int32_t red[4 * NW];
     // bias only: the head's positional table and each stage's key timestamps
     // (at least 64 entries: one wave-load)
     constexpr int TSN = RAB ? (BN < 64 ? 64 : BN) : 1;
@@ -637,7 +613,29 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
     // One work item (sequence, head, q-tile, split) from plan to output.
     auto run_item = [&](const KernelParams &p, const WorkItem &item) __attribute__((always_inline)) {
         BlockPlan bp;
-        if (!plan_block<BN, NW>(p, SPLIT, bp, red, item)) return;
+        const bool planned = plan_block<BN, NW>(p, SPLIT, bp, item);
+        // heavy q-tiles: the chunk of this item (hslot >= 0 when the q-tile is cut);
+        // the first chunk's work-group records the q-tile for the combine pass
+        int32_t hslot = -1;
+        if (!SPLIT && p.heavy) {
+            const int64_t hq = ((int64_t)item.b * p.H + item.h) * p.num_qt + item.qt;
+            int32_t nsp = 0;
+            if (planned) nsp = heavy_splits(bp.tiles.count(), BN);
+            if (item.valid && item.sp == 0 && threadIdx.x == 0) {
+                const int32_t r0 = item.qt * C::BM;
+                const int32_t rows = planned ? imin(C::BM, bp.s.S_q - r0) : 0;
+                p.hmeta[2 * hq] = nsp | (rows << 8);
+                p.hmeta[2 * hq + 1] = planned ? (int32_t)(bp.s.q0 + r0) : 0;
+            }
+            if (!planned || item.sp >= nsp) return;
+            if (nsp > 1) {
+                int32_t nb, ne;
+                heavy_chunk(bp.tiles.count(), nsp, item.sp, &nb, &ne);
+                bp.tiles = bp.tiles.sub(nb, ne);
+                hslot = (int32_t)(hq * p.num_splits + item.sp);
+            }
+        }
+        if (!planned) return;
         const SeqGeom &s = bp.s;
         const RowSpan &span = bp.span;
         // the lane's constants are derived per item (an opaque copy of the thread
@@ -993,6 +991,27 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         // staged store below; only its row is not written)
         if (SPLIT && !span.valid) return;
         const int64_t grow = s.q0 + bp.row;  // token row of o
+        if (!SPLIT && hslot >= 0) {
+            // a chunk of a cut q-tile: fp32 partial rows, scaled like the split-KV
+            // partials; the combine pass adds the chunks up (softmax: by their LSEs)
+            if (!span.valid) return;
+            const int64_t prow = (int64_t)hslot * C::BM + (bp.row - bp.it.qt * C::BM);
+            float *pp = p.hpart_o + prow * DV + 4 * g;
+#pragma unroll
+            for (int nb = 0; nb < C::NDB; ++nb) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x16_t &a = oacc[nb];
+                    *(f32x4_t *)(pp + nb * 32 + 8 * i4) =
+                        f32x4_t{a[4 * i4] * scale, a[4 * i4 + 1] * scale, a[4 * i4 + 2] * scale,
+                                a[4 * i4 + 3] * scale};
+                }
+            }
+            if constexpr (SOFTMAX) {
+                if (g == 0) p.hpart_lse[prow] = lse_val;
+            }
+            return;
+        }
         if constexpr (!SPLIT) {
             // The wave's 32 output rows go through LDS (both ring stages are free
             // once the last tile's barrier has passed; each wave uses a region of
@@ -1191,6 +1210,80 @@ __global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D
     }
 }
 
+// Combine pass of the cut (heavy) q-tiles: kHeavyCombineBlocks work-groups per
+// q-tile, each over a run of its rows; a q-tile that was not cut (chunk count < 2)
+// or lies past its sequence is skipped.  A thread takes 4 columns of a row, loads
+// every chunk's partial (and LSE) before using any, and adds them in chunk order
+// (SiLU: a sum; softmax: weights exp(lse_c - lse) as in the split-KV combine),
+// then writes o (and the LSE).
+constexpr int kHeavyCombineBlocks = 8;
+template <int DT, bool SOFTMAX, int BM>
+__global__ __launch_bounds__(256) void hstu_heavy_combine_kernel(KernelParams p, int D) {
+    using E = Elem<DT>;
+    const int64_t hq = blockIdx.x / kHeavyCombineBlocks;
+    const int part = blockIdx.x % kHeavyCombineBlocks;
+    const int64_t bh = hq / p.num_qt;
+    if (bh >= (int64_t)p.B * p.H) return;
+    const int32_t meta = p.hmeta[2 * hq], tok0 = p.hmeta[2 * hq + 1];
+    const int nsp = meta & 255, rows = meta >> 8;
+    if (nsp < 2) return;
+    const int h = (int)(bh % p.H);
+    const int nchunk = D / 4;
+    constexpr int RPB = BM / kHeavyCombineBlocks;  // rows of this work-group
+    const int64_t slot0 = hq * p.num_splits;
+    for (int idx = threadIdx.x; idx < RPB * nchunk; idx += 256) {
+        const int row = part * RPB + idx / nchunk, c4 = idx % nchunk;
+        if (row >= rows) break;
+        f32x4_t v[kHeavyMaxSplits];
+        float l[kHeavyMaxSplits];
+#pragma unroll
+        for (int c = 0; c < kHeavyMaxSplits; ++c) {
+            const bool in = c < nsp;
+            const int64_t prow = (slot0 + c) * BM + row;
+            v[c] = in ? *(const f32x4_t *)(p.hpart_o + prow * D + c4 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (SOFTMAX) l[c] = in ? p.hpart_lse[prow] : -INFINITY;
+        }
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float lse = 0.f;
+        if constexpr (!SOFTMAX) {
+#pragma unroll
+            for (int c = 0; c < kHeavyMaxSplits; ++c) acc += v[c];
+        } else {
+            float m = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < kHeavyMaxSplits; ++c) m = fmaxf(m, l[c]);
+            if (m == -INFINITY) {
+                lse = -INFINITY;  // no chunk saw a key: o = 0
+            } else {
+                float sum = 0.f;
+#pragma unroll
+                for (int c = 0; c < kHeavyMaxSplits; ++c) {
+                    const float wc = __builtin_amdgcn_exp2f((l[c] - m) * kLog2e);  // 0 for absent chunks
+                    sum += wc;
+                    acc += wc * v[c];
+                }
+                acc *= __builtin_amdgcn_rcpf(sum);
+                lse = m + __builtin_amdgcn_logf(sum) * kLn2;
+            }
+        }
+        const int64_t grow = (int64_t)tok0 + row;
+        uint16_t *op = (uint16_t *)p.o + grow * p.o_stride + h * D + c4 * 4;
+        *(u32x2_t *)op = u32x2_t{E::pack2(acc[0], acc[1]), E::pack2(acc[2], acc[3])};
+        if constexpr (SOFTMAX) {
+            if (p.lse != nullptr && c4 == 0) {
+                int64_t li;
+                if (p.jagged) {
+                    li = (int64_t)h * p.total_rows + grow;
+                } else {
+                    const int64_t b = grow / p.seqlen_q, i = grow % p.seqlen_q;
+                    li = (b * p.H + h) * p.seqlen_q + i;
+                }
+                p.lse[li] = lse;
+            }
+        }
+    }
+}
+
 // Visible pairs inside the scheduled key tiles, counted with the forward
 // kernel's own plan, lane -> (row, key) assignment and tile classes: a tile the
 // work-group-level test (BlockPlan::tile_full, which sends a tile through the
@@ -1202,9 +1295,8 @@ __global__ __launch_bounds__(256) void hstu_combine_kernel(KernelParams p, int D
 // comparison with an independently computed count of the mask's visible pairs.
 template <int BN, int NW>
 __global__ __launch_bounds__(64 * NW) void hstu_count_kernel(KernelParams p, unsigned long long *count) {
-    __shared__ int32_t red[4 * NW];
     BlockPlan bp;
-    if (!plan_block<BN, NW>(p, false, bp, red, decode_work(p, blockIdx.x))) return;
+    if (!plan_block<BN, NW>(p, false, bp, decode_work(p, blockIdx.x))) return;
     const int lane = threadIdx.x & 63, g = lane >> 5;
     unsigned long long mine = 0;
     const int ntiles = bp.tiles.count();
@@ -1484,6 +1576,25 @@ hipError_t launch_combine(const KernelParams &p, int dtype, int D, bool softmax,
             hipLaunchKernelGGL((hstu_combine_kernel<HSTU_FP16, true>), dim3(blocks), dim3(256), 0, stream, p, D);
         else
             hipLaunchKernelGGL((hstu_combine_kernel<HSTU_FP16, false>), dim3(blocks), dim3(256), 0, stream, p, D);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_heavy_combine(const KernelParams &p, int dtype, int D, int DV, bool softmax, hipStream_t stream) {
+    const int64_t blocks = (int64_t)p.bh_pad * p.num_qt * kHeavyCombineBlocks;
+    if (blocks <= 0) return hipSuccess;
+    const int bm = block_m_for(D);
+    if (bm != 128) return hipErrorInvalidValue;
+    if (dtype == HSTU_BF16) {
+        if (softmax)
+            hipLaunchKernelGGL((hstu_heavy_combine_kernel<HSTU_BF16, true, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, p, DV);
+        else
+            hipLaunchKernelGGL((hstu_heavy_combine_kernel<HSTU_BF16, false, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, p, DV);
+    } else {
+        if (softmax)
+            hipLaunchKernelGGL((hstu_heavy_combine_kernel<HSTU_FP16, true, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, p, DV);
+        else
+            hipLaunchKernelGGL((hstu_heavy_combine_kernel<HSTU_FP16, false, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, p, DV);
     }
     return hipGetLastError();
 }

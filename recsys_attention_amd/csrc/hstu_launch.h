@@ -15,10 +15,17 @@ constexpr int key_tile_for(int D) { return D <= 64 ? 128 : (D <= 128 ? 64 : 32);
 // since the CU-wide barrier keeps the two waves of each SIMD in the same phase.
 constexpr int waves_for(int) { return 4; }
 constexpr int block_m_for(int D) { return 32 * waves_for(D); }
+// Work-groups of the forward kernel resident per CU (its occupancy bound: two
+// waves per SIMD, one for hdim 256) and the CUs of an MI355X: a per-item grid of
+// fewer work-groups than their product leaves CUs idle.
+constexpr int groups_per_cu_for(int D) { return D >= 256 ? 1 : 2; }
+constexpr int kChipCUs = 256;
 
 hipError_t launch_forward(const KernelParams &p, int dtype, int D, int DV, bool softmax, bool split,
                           hipStream_t stream);
 hipError_t launch_combine(const KernelParams &p, int dtype, int D, bool softmax, hipStream_t stream);
+// combine pass of the cut (heavy) q-tiles of an unsplit call on the per-item grid
+hipError_t launch_heavy_combine(const KernelParams &p, int dtype, int D, int DV, bool softmax, hipStream_t stream);
 hipError_t launch_count(const KernelParams &p, int D, unsigned long long *count, hipStream_t stream);
 
 // The allocation-free entry point's static scratch (HSTU_NOALLOC_SCRATCH_BYTES,

@@ -43,6 +43,16 @@ struct KernelParams {
     // the planning kernel before the launch; nullptr: one work item per
     // work-group, the work-group id
     uint32_t *queue;
+    // heavy q-tiles (per-item grid, unsplit call): when set, num_splits is the
+    // largest chunk count and the split index of a work item picks its chunk of
+    // a cut q-tile's key-tile list; the chunks' fp32 partial results (and LSEs)
+    // go to hpart_o [slot][BM rows][Dv] and hpart_lse [slot][BM rows], slot =
+    // ((b H + h) num_qt + qt) num_splits + chunk; hmeta [(b H + h) num_qt + qt][2]
+    // holds the q-tile's chunk count | valid rows << 8 and its first token
+    int32_t heavy;
+    float *hpart_o;
+    float *hpart_lse;
+    int32_t *hmeta;
 };
 
 // Work queues of the persistent schedule, in the caller's workspace:

@@ -164,6 +164,45 @@ HSTU_HD BlockBand block_band_join(const BlockBand &a, const BlockBand &b) {
     return BlockBand{imin(a.lo, b.lo), imax(a.hi, b.hi), imax(a.full_lo, b.full_lo), imin(a.full_hi, b.full_hi)};
 }
 
+// The BlockBand of rows [r0, r1] of a sequence (rows past the sequence count as
+// rows without a band that constrain nothing) without visiting every row.  The
+// rows fall into four regions: context, UIH rows before the min-full tail, the
+// min-full tail, targets.  Inside a region the row's x (its position against the
+// key history) is constant or grows with the row, and lo and hi are
+// non-decreasing in x; the rows whose band is empty are those with x below a
+// threshold (causal: x < 0; otherwise, outside full rows: x < -local_len), so a
+// prefix of the region.  Hence a region's rows contribute exactly what its first
+// row, its first row with a band and its last row contribute: the union is the
+// first non-empty row's lo and the last row's hi, and the intersection is empty
+// when the first row's band is, else [last row's lo, first row's hi].  Equal to
+// joining row_band over every row of the range.
+HSTU_HD BlockBand qtile_band(const SeqGeom &s, int32_t causal, int32_t r0, int32_t r1) {
+    BlockBand u = block_band_init();
+    r0 = imax(r0, 0);
+    r1 = imin(r1, s.S_q - 1);
+    if (r0 > r1) return u;
+    const int32_t uih0 = s.Cq, tgt0 = s.Cq + s.Uq;
+    const int32_t tail0 = s.M > 0 ? imax(uih0, tgt0 - s.M) : tgt0;  // first min-full row
+    const int32_t start[5] = {0, uih0, tail0, tgt0, s.S_q};
+    for (int k = 0; k < 4; ++k) {
+        const int32_t a = imax(r0, start[k]), b = imin(r1, start[k + 1] - 1);
+        if (a > b) continue;
+        u = block_band_join(u, row_band(row_span(s, causal, a)));
+        u = block_band_join(u, row_band(row_span(s, causal, b)));
+        if (k == 1 || k == 2) {
+            // UIH rows: x = row - Cq + Ukv - Uq; the first row with a band has
+            // x >= 0 (causal) or x >= -L (non-causal rows that are not full)
+            const bool full = s.L == 0 || k == 2;
+            if (causal || !full) {
+                const int32_t x_min = causal ? 0 : -s.L;
+                const int32_t first = imax(a, x_min + s.Cq + s.Uq - s.Ukv);
+                if (first > a && first <= b) u = block_band_join(u, row_band(row_span(s, causal, first)));
+            }
+        }
+    }
+    return u;
+}
+
 // Key tile [j0, j0 + BN) is visible to every valid row of the work-group: it lies
 // in the context prefix [0, ctx), or its part past the prefix lies inside every
 // valid row's band.  (A work-group with no valid row has full_lo > full_hi.)
@@ -197,6 +236,16 @@ struct TileList {
     int32_t b0, b1; // second range [b0, b1)
     HSTU_HD int32_t count() const { return (a1 - a0) + (b1 - b0); }
     HSTU_HD int32_t at(int32_t n) const { return n < a1 - a0 ? a0 + n : b0 + (n - (a1 - a0)); }
+    // the tiles at positions [nb, ne) (0 <= nb <= ne <= count()), as a list
+    HSTU_HD TileList sub(int32_t nb, int32_t ne) const {
+        const int32_t na = a1 - a0;
+        TileList t;
+        t.a0 = a0 + imin(nb, na);
+        t.a1 = a0 + imin(ne, na);
+        t.b0 = b0 + imax(nb - na, 0);
+        t.b1 = b0 + imax(ne - na, 0);
+        return t;
+    }
 };
 
 HSTU_HD TileList make_tile_list(int32_t ctx, bool any_valid_row, int32_t band_lo, int32_t band_hi,
@@ -219,6 +268,27 @@ HSTU_HD TileList make_tile_list(int32_t ctx, bool any_valid_row, int32_t band_lo
     t.b1 = imin(bb, t_end);
     if (t.b1 < t.b0) t.b1 = t.b0;
     return t;
+}
+
+// Heavy q-tiles (per-item grid): a q-tile whose key-tile list is long is cut into
+// up to kHeavyMaxSplits contiguous chunks of its list, each processed by a work-
+// group of its own, so that no single work-group walks a whole long history (the
+// q-tile holding a sequence's min-full and target rows under a local window, the
+// last q-tiles of a long causal sequence).  A chunk holds at least 256 keys'
+// worth of tiles; a q-tile of at most that many tiles is not cut.
+constexpr int32_t kHeavyMaxSplits = 4;
+HSTU_HD int32_t heavy_chunk_tiles(int32_t BN) { return BN >= 256 ? 1 : 256 / BN; }
+HSTU_HD int32_t heavy_splits(int32_t ntiles, int32_t BN) {
+    const int32_t t = heavy_chunk_tiles(BN);
+    if (ntiles <= t) return 1;
+    return imin(kHeavyMaxSplits, (ntiles + t - 1) / t);
+}
+// Positions [n_begin, n_end) of chunk sp of a list of ntiles tiles cut into nsp
+// chunks whose sizes differ by at most one (earlier chunks the larger).
+HSTU_HD void heavy_chunk(int32_t ntiles, int32_t nsp, int32_t sp, int32_t *n_begin, int32_t *n_end) {
+    const int32_t q = ntiles / nsp, r = ntiles % nsp;
+    *n_begin = sp * q + imin(sp, r);
+    *n_end = *n_begin + q + (sp < r ? 1 : 0);
 }
 
 // Tiles [t_begin, t_end) of split sp: the sequence's key tiles cut into
@@ -249,6 +319,22 @@ struct WorkItem {
 HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
     WorkItem it;
     int64_t bh, rest;
+    if (p.heavy) {
+        // chunk-major: every q-tile's first chunk (the whole q-tile when it is not
+        // cut) comes first, in the schedule-2 order, then the second chunks, ...,
+        // so that the work-groups of chunks a q-tile does not have (most of them)
+        // come after all first chunks
+        const int64_t per_sp = (int64_t)p.bh_pad * p.num_qt;
+        it.sp = (int32_t)(w / per_sp);
+        const int64_t v = w % per_sp;
+        const int64_t xcd = v % 8, loc = v / 8;
+        bh = (loc / p.num_qt) * 8 + xcd;
+        it.qt = p.num_qt - 1 - (int32_t)(loc % p.num_qt);
+        it.b = (int32_t)(bh / p.H);
+        it.h = (int32_t)(bh % p.H);
+        it.valid = bh < (int64_t)p.B * p.H;
+        return it;
+    }
     if (p.schedule >= 2) {
         const int64_t xcd = w % 8, loc = w / 8;
         const int64_t per_bh = (int64_t)p.num_qt * p.num_splits;

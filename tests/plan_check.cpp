@@ -15,11 +15,16 @@
 //   row classes     tile_state EMPTY: no visible key of the row in the tile; FULL:
 //                   every key of the tile exists and is visible; rows past the
 //                   sequence are EMPTY;
+//   closed form     qtile_band gives the q-tile's joined row bands (union and
+//                   intersection) exactly;
 //   work-group test block_tile_full (the pipelined body's unmasked tiles): every
 //                   valid row of the q-tile sees every key of the tile;
 //   lane masks      lane_key_mask (the pipelined body's masked tiles): bit e is
 //                   set exactly when the row sees key jb + 8 (e / 4) + e % 4, for
 //                   64-key tiles and both lane groups' first keys;
+//   heavy chunks    heavy_splits / heavy_chunk / TileList::sub cut a q-tile's list
+//                   into at most kHeavyMaxSplits non-empty runs of consecutive
+//                   positions that concatenate to the list;
 //   splits          split_range cuts [0, nt) into contiguous, disjoint ranges
 //                   that cover it (1 .. 6 splits and 16), and the per-split tile
 //                   lists concatenate to the unsplit list;
@@ -115,6 +120,10 @@ void check_case(const Case &c) {
                 rows[k] = row_span(s, c.causal, r0 + k);
                 band = block_band_join(band, row_band(rows[k]));
             }
+            // closed form: the same four terms from at most twelve rows
+            const BlockBand qb = qtile_band(s, c.causal, r0, r0 + BM - 1);
+            if (qb.lo != band.lo || qb.hi != band.hi || qb.full_lo != band.full_lo || qb.full_hi != band.full_hi)
+                fail("qtile_band differs from the rows' joined band", r0, BM, qb.lo - band.lo);
             const TileList tl = make_tile_list(s.Ck, true, band.lo, band.hi, BN, 0, nt);
             std::vector<char> in_list(nt > 0 ? nt : 1, 0);
             int prev = -1;
@@ -164,6 +173,27 @@ void check_case(const Case &c) {
                         for (int j = j0; j < j1; ++j) counted += span_visible(r, j) ? 1 : 0;
                     }
                 }
+            }
+            // heavy q-tile chunks: sub-lists of consecutive positions that
+            // concatenate to the list, at most kHeavyMaxSplits of them, none empty
+            {
+                const int cnt = tl.count();
+                const int nsp = heavy_splits(cnt, BN);
+                if (nsp < 1 || nsp > kHeavyMaxSplits || (nsp > 1 && cnt <= heavy_chunk_tiles(BN)))
+                    fail("heavy split count", cnt, nsp);
+                int expect = 0;
+                for (int sp = 0; sp < nsp; ++sp) {
+                    int32_t nb = -1, ne = -1;
+                    heavy_chunk(cnt, nsp, sp, &nb, &ne);
+                    if (nb != expect || ne < nb || ne > cnt || (cnt > 0 && ne == nb))
+                        fail("heavy chunks do not partition the list", cnt, sp, nb);
+                    const TileList sl = tl.sub(nb, ne);
+                    if (sl.count() != ne - nb) fail("sub-list size", cnt, nb, ne);
+                    for (int k = 0; k < sl.count(); ++k)
+                        if (sl.at(k) != tl.at(nb + k)) fail("sub-list tile differs", cnt, nb + k, sl.at(k));
+                    expect = ne;
+                }
+                if (expect != cnt) fail("heavy chunks do not reach the end of the list", cnt, expect);
             }
             // split-KV: contiguous ranges covering [0, nt); lists concatenate
             for (int ns : kSplits) {

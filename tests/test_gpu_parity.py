@@ -251,7 +251,10 @@ def test_jagged_equal_lengths_equals_batched():
 
 def test_group_equals_separate_calls():
     w = W.config("group4_silu_bf16_d256")
-    full = o_tokens(w, DeviceInputs(w).forward())
+    # an explicit schedule (the per-item grid) on both sides: left to the library,
+    # the small per-group calls would cut their long q-tiles into chunks, which
+    # adds the same terms in another order
+    full = o_tokens(w, DeviceInputs(w).forward(schedule=2))
     per = w.batch // len(w.groups)
     for g in range(len(w.groups)):
         bs = list(range(g * per, (g + 1) * per))
@@ -263,7 +266,7 @@ def test_group_equals_separate_calls():
         sub.q_bits, sub.k_bits, sub.v_bits = w.q_bits[t0:t1], w.k_bits[t0:t1], w.v_bits[t0:t1]
         # a single group's default scale uses the group's own max, which the full
         # call also uses, so the outputs must agree bit for bit
-        got = o_tokens(sub, DeviceInputs(sub).forward())
+        got = o_tokens(sub, DeviceInputs(sub).forward(schedule=2))
         assert np.array_equal(got, full[t0:t1])
 
 
@@ -324,3 +327,28 @@ def test_self_equals_cross_on_context_and_history_prefix(softmax, local_len, con
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     else:
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_heavy_qtiles_cut_into_chunks(case):
+    """Unsplit calls left to the library on a grid too small for the persistent
+    schedule cut the q-tiles with long key-tile lists (the min-full and target rows
+    under a local window, the tail of a causal sequence) into chunks on separate
+    work-groups, combined afterwards (CK README "Split-KV", applied per q-tile).
+    Against the oracle, and against the uncut per-item grid (schedule 2) within the
+    same tolerance; pair counts exact."""
+    d, dv, softmax, L, M = [(128, 128, False, 5, 6), (128, 128, True, 5, 6), (256, 256, False, 0, 0),
+                            (64, 64, True, 8, 16), (96, 64, False, 3, 9), (128, 128, False, 0, 0)][case]
+    groups = [W.MaskGroup(L, 6, M, 0.0)]
+    w = W.build("heavy", dtype="bf16" if case % 2 == 0 else "fp16", batch=3, nhead=2, hdim_qk=d, hdim_v=dv,
+                jagged=True, cross=False, causal=True, softmax=softmax, alpha=0.0, groups=groups,
+                uih_q=[1500, 700, 90], targets=[6, 3, 1], seed=300 + case)
+    stats = _check_full(w, schedule=0)
+    dev = DeviceInputs(w)
+    a, b = dev.forward(schedule=0), dev.forward(schedule=2)
+    torch.cuda.synchronize()
+    oa = o_tokens(w, a[0] if softmax else a)
+    ob = o_tokens(w, b[0] if softmax else b)
+    compare(oa, ob, w.dtype, "cut vs uncut")
+    if softmax:
+        compare_lse(lse_tokens(w, a[1]), lse_tokens(w, b[1]), "cut vs uncut")

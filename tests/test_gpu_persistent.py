@@ -210,7 +210,11 @@ def test_planned_queues_hold_every_item_once_in_order(batch, nhead, maxlen):
     torch.cuda.synchronize()
     raw = ws.cpu().numpy()
     header = raw[:256].view(np.uint32)
-    per_queue = (need - 256) // 64
+    # one entry per possible item (8 queues of (b, h) pairs x q-tiles); the
+    # workspace may hold more after the queues (a small unsplit grid: room for
+    # cutting heavy q-tiles when the library picks the schedule)
+    per_queue = (batch * nhead + 7) // 8 * ((w.max_seqlen_q + 127) // 128)
+    assert need >= 256 + 64 * per_queue
     lists = raw[256:256 + 64 * per_queue].view(np.uint64).reshape(8, per_queue)
     queues, counts = _expected_queues(w, per_queue)
     for x in range(8):
