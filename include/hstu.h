@@ -80,7 +80,10 @@ typedef struct {
     int32_t context_len; /* always-visible prefix length */
     int32_t minfull_len; /* tail of the UIH that attends the full history; 0 disables */
     float attn_scale;    /* post-non-linearity scale; 0 selects 1 / max(max_uih_q, 1) */
-    int32_t max_uih_q;   /* largest UIH query length in the group; read only when attn_scale == 0 */
+    int32_t max_uih_q;   /* largest UIH query length in the group; read only when attn_scale == 0.
+                          * (CK README "Command-line arguments": an attn_scale of 0 means one over
+                          * the max UIH length, derived there from the host-side lengths; here the
+                          * lengths live on the device, so the caller states it, and 0 gives 1.) */
 } hstu_mask_group_t;
 
 typedef struct {
@@ -134,18 +137,34 @@ typedef struct {
     int32_t rab_pos_len;           /* 1 ..= HSTU_RAB_MAX_POS when rab_pos is set */
 } hstu_fwd_args_t;
 
-/* Host-only argument check (no HIP call); also run by every entry point. */
+/* Host-only argument check (no HIP call); also run by every entry point.  It covers
+ * the operator's arguments as CK README "Command-line arguments" lists them (dtype,
+ * batch and groups, jagged mode, heads, head dims, lengths, targets, softmax, causal,
+ * the mask lengths, alpha and attn_scale) plus this boundary's own (pointers,
+ * strides, alignment, schedule, bias).  Returns HSTU_OK, HSTU_ERR_INVALID_ARG (a
+ * value out of its domain) or HSTU_ERR_UNSUPPORTED (valid, not built: a head-dim
+ * pair, bias with cross-attention); hstu_last_error() then names the argument.
+ * Reads args only; NULL args is HSTU_ERR_INVALID_ARG. */
 hstu_status_t hstu_validate_args(const hstu_fwd_args_t *args);
 
 /* Bytes of workspace for num_splits splits (num_splits == 1: hstu_fwd): the split-KV
- * partial results, plus, when args->schedule is 0 or 3, the work queues (256 bytes
- * and 8 per possible item: batch * nhead rounded up to 8, times the q-tiles of
- * max_seqlen_q in 128 rows, times num_splits).  Returns 0 on invalid arguments. */
+ * partial results (README "Split-KV": fp32 partial rows and, for softmax, their LSEs),
+ * plus, when args->schedule is 0 or 3, the work queues (256 bytes and 8 per possible
+ * item: batch * nhead rounded up to 8, times the q-tiles of max_seqlen_q in 128 rows,
+ * times num_splits), plus, for an unsplit call with schedule 0 whose per-item grid
+ * is smaller than the chip's resident work-groups, room for cutting long q-tiles
+ * into chunks (4 fp32 partials of 128 rows per q-tile, their LSEs for softmax, and
+ * 8 bytes per q-tile; at most 512 MiB, else the room is left out and nothing is
+ * cut).  Host-only; returns 0 on invalid arguments. */
 size_t hstu_fwd_workspace_size(const hstu_fwd_args_t *args, int32_t num_splits);
 
 /* The forward operator: one fused kernel per call (plus, for schedule 3, an 8-work-
- * group kernel that writes the work queues).  ws may be NULL: then schedule 0 runs
- * as 2, and schedule 3 fails with HSTU_ERR_WORKSPACE.  A workspace of at least
+ * group kernel that writes the work queues; plus, when long q-tiles are cut into
+ * chunks, a combine kernel).  ws may be NULL: then schedule 0 runs as 2, and
+ * schedule 3 fails with HSTU_ERR_WORKSPACE.  Schedule 0 on a small per-item grid
+ * runs the q-tiles in levels from each sequence's end, and, with room in ws, cuts
+ * q-tiles of more than 256 keys' worth of key tiles into up to 4 chunks whose fp32
+ * partials a combine kernel adds up (same terms, another order of addition).  A workspace of at least
  * hstu_fwd_workspace_size(args, 1) bytes, 16-byte aligned, is used by schedule 0
  * and 3; its contents need no initialisation; calls that share a workspace must
  * not overlap in time. */
@@ -168,7 +187,8 @@ hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, 
  * array of HSTU_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
  * on until the process ends.  The caller passes inputs and outputs as for
  * hstu_fwd_splitkv; the call allocates and frees nothing.  A problem whose
- * workspace (hstu_fwd_workspace_size) exceeds the scratch is rejected with
+ * workspace (hstu_fwd_workspace_size without the room for chunks of long q-tiles,
+ * which this entry point never cuts) exceeds the scratch is rejected with
  * HSTU_ERR_WORKSPACE before anything runs.  All calls on one GPU share its
  * scratch (each call's kernels overwrite what they use; nothing needs to start at
  * zero): calls that overlap in time on one GPU (other streams, other threads)
@@ -178,8 +198,13 @@ hstu_status_t hstu_fwd_splitkv_noalloc(const hstu_fwd_args_t *args, int32_t num_
 
 /* Counts, on the device, the visible (b, h, i, j) pairs inside the key tiles the
  * forward kernel schedules, with the kernel's own mask predicate.  Equal to the
- * number of visible pairs of the mask exactly when no skipped tile holds one.
- * d_count: device pointer to one uint64, overwritten (zeroed by the library). */
+ * number of visible pairs of the mask exactly when no skipped tile holds one: the
+ * check CK README "Test / Verify" makes against a CPU reference, here on the mask
+ * alone, and the FLOP count of README "Benchmark" (the two GEMMs) restricted to
+ * visible pairs.  d_count: device pointer to one uint64, overwritten (zeroed by
+ * the library on the stream first); the call returns before the count is ready
+ * (read it after synchronising hip_stream).  Errors as hstu_validate_args, plus
+ * HSTU_ERR_INVALID_ARG for a NULL d_count and HSTU_ERR_HIP for a failed launch. */
 hstu_status_t hstu_count_visible_pairs(const hstu_fwd_args_t *args, unsigned long long *d_count,
                                        void *hip_stream);
 

@@ -190,7 +190,7 @@ constexpr int64_t kPersistentItems = 2048;
 // Heavy q-tiles.  When the per-item grid of an unsplit call (schedule left to
 // the library) holds fewer work-groups than the chip runs at once, the kernel's
 // time is that of its heaviest q-tile; the q-tiles with more than a chunk of key
-// tiles (heavy_chunk_tiles) are then cut into chunks that run side by side, and
+// tiles (heavy_tiles_for) are then cut into chunks that run side by side, and
 // a combine pass adds the chunks' partials up.  The workspace holds the partials
 // (kHeavyMaxSplits per q-tile) and each q-tile's record, after the rest.
 constexpr size_t kHeavyMaxBytes = (size_t)512 << 20;
@@ -198,6 +198,7 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 size_t base_workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     return partial_bytes(a, num_splits) + (wants_queue(a) ? queue_bytes(a, num_splits) : 0);
 }
+int32_t heavy_tiles_for(const hstu_fwd_args_t *a) { return hstu::heavy_chunk_tiles(hstu::key_tile_for(a->hdim_qk)); }
 size_t heavy_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     if (a->schedule != 0 || num_splits != 1) return 0;
     hstu::KernelParams p;
@@ -206,7 +207,7 @@ size_t heavy_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     if (items >= kPersistentItems || items >= (int64_t)hstu::kChipCUs * hstu::groups_per_cu_for(a->hdim_qk))
         return 0;
     const int32_t bn = hstu::key_tile_for(a->hdim_qk);
-    if ((p.seqlen_kv + bn - 1) / bn <= hstu::heavy_chunk_tiles(bn)) return 0;  // no q-tile is cut
+    if ((p.seqlen_kv + bn - 1) / bn <= heavy_tiles_for(a)) return 0;  // no q-tile is cut
     const size_t qtiles = (size_t)items;
     const size_t rows = qtiles * hstu::kHeavyMaxSplits * (size_t)hstu::block_m_for(a->hdim_qk);
     const size_t b = align256(rows * (size_t)a->hdim_v * sizeof(float)) +
@@ -292,6 +293,9 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
     if ((st = check_grid(p)) != HSTU_OK) return st;
     if ((st = pick_schedule(args, 1, ws, ws_bytes, p)) != HSTU_OK) return st;
     if (p.total_rows == 0 || p.B == 0) return HSTU_OK;
+    // a small per-item grid left to the library runs in q-tile levels from each
+    // sequence's end (the heaviest q-tiles dispatched first)
+    if (args->schedule == 0 && p.queue == nullptr && hstu::grid_size(p) < kPersistentItems) p.levels = 1;
     // heavy q-tiles cut into chunks when the per-item grid runs and the workspace
     // holds the chunks' partials (hstu_fwd_workspace_size counts them)
     const size_t heavy = heavy_bytes(args, 1);
@@ -300,6 +304,7 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
         const size_t qtiles = (size_t)p.bh_pad * (size_t)p.num_qt;
         const size_t rows = qtiles * hstu::kHeavyMaxSplits * (size_t)hstu::block_m_for(args->hdim_qk);
         p.heavy = 1;
+        p.heavy_tiles = heavy_tiles_for(args);
         p.num_splits = hstu::kHeavyMaxSplits;
         p.hpart_o = (float *)h;
         h += align256(rows * (size_t)args->hdim_v * sizeof(float));

@@ -124,6 +124,12 @@ __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, Bl
     bp.it = item;
     if (!bp.it.valid) return false;
     bp.s = seq_geom(p, bp.it.b);
+    if (p.levels && p.queue == nullptr) {
+        // level l counted from the sequence's last q-tile: q-tile nq - 1 - l, and
+        // the levels past the sequence onto the q-tiles past it (one to one)
+        const int32_t nq = (bp.s.S_q + 32 * NW - 1) / (32 * NW), l = bp.it.qt;
+        bp.it.qt = l < nq ? nq - 1 - l : l;
+    }
     const int32_t r0 = bp.it.qt * (32 * NW);
     if (r0 >= bp.s.S_q) return false;
     bp.row = r0 + wave * 32 + (lane & 31);
@@ -618,11 +624,11 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         // the first chunk's work-group records the q-tile for the combine pass
         int32_t hslot = -1;
         if (!SPLIT && p.heavy) {
-            const int64_t hq = ((int64_t)item.b * p.H + item.h) * p.num_qt + item.qt;
+            const int64_t hq = ((int64_t)item.b * p.H + item.h) * p.num_qt + bp.it.qt;
             int32_t nsp = 0;
-            if (planned) nsp = heavy_splits(bp.tiles.count(), BN);
+            if (planned) nsp = heavy_splits(bp.tiles.count(), p.heavy_tiles);
             if (item.valid && item.sp == 0 && threadIdx.x == 0) {
-                const int32_t r0 = item.qt * C::BM;
+                const int32_t r0 = bp.it.qt * C::BM;
                 const int32_t rows = planned ? imin(C::BM, bp.s.S_q - r0) : 0;
                 p.hmeta[2 * hq] = nsp | (rows << 8);
                 p.hmeta[2 * hq + 1] = planned ? (int32_t)(bp.s.q0 + r0) : 0;
@@ -1042,12 +1048,21 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             constexpr int RPI = 64 / LPR;  // rows per store instruction
             const int c = lane % LPR;
             const int64_t wtok = s.q0 + (int64_t)wrow0;  // token of the wave's first row
+            // every read back first, then the stores; the output's base and stride
+            // in registers (read from the arguments after a store, they would be
+            // reloaded, and waited for, before each store)
+            u32x4_t v[32 / RPI];
 #pragma unroll
             for (int k = 0; k < 32 / RPI; ++k) {
                 const int r = k * RPI + lane / LPR;
-                const u32x4_t v = *(const u32x4_t *)(stg + r * PITCH + ((c ^ (r & SWZ)) * 16));
-                if (c < CH && wrow0 + r < s.S_q)
-                    *(u32x4_t *)((uint16_t *)p.o + (wtok + r) * p.o_stride + h * DV + c * 8) = v;
+                v[k] = *(const u32x4_t *)(stg + r * PITCH + ((c ^ (r & SWZ)) * 16));
+            }
+            uint16_t *const o_row = (uint16_t *)p.o + wtok * p.o_stride + h * DV + c * 8;
+            const int64_t o_stride = p.o_stride;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int r = k * RPI + lane / LPR;
+                if (c < CH && wrow0 + r < s.S_q) *(u32x4_t *)(o_row + r * o_stride) = v[k];
             }
             if constexpr (SOFTMAX) {
                 if (p.lse != nullptr && g == 0 && span.valid) {

@@ -43,13 +43,19 @@ struct KernelParams {
     // the planning kernel before the launch; nullptr: one work item per
     // work-group, the work-group id
     uint32_t *queue;
-    // heavy q-tiles (per-item grid, unsplit call): when set, num_splits is the
-    // largest chunk count and the split index of a work item picks its chunk of
-    // a cut q-tile's key-tile list; the chunks' fp32 partial results (and LSEs)
-    // go to hpart_o [slot][BM rows][Dv] and hpart_lse [slot][BM rows], slot =
-    // ((b H + h) num_qt + qt) num_splits + chunk; hmeta [(b H + h) num_qt + qt][2]
-    // holds the q-tile's chunk count | valid rows << 8 and its first token
+    // per-item grid of an unsplit call: work-group ids run over q-tile levels
+    // counted from each sequence's end (decode_work), so that the last q-tile of
+    // every sequence, the heaviest under a causal mask, is dispatched first
+    int32_t levels;
+    // heavy q-tiles (with levels): when set, num_splits is the largest chunk
+    // count and the split index of a work item picks its chunk of a q-tile's
+    // key-tile list, cut into chunks of at least heavy_tiles tiles; the chunks'
+    // fp32 partial results (and LSEs) go to hpart_o [slot][BM rows][Dv] and
+    // hpart_lse [slot][BM rows], slot = ((b H + h) num_qt + qt) num_splits +
+    // chunk; hmeta [(b H + h) num_qt + qt][2] holds the q-tile's chunk count |
+    // valid rows << 8 and its first token
     int32_t heavy;
+    int32_t heavy_tiles;
     float *hpart_o;
     float *hpart_lse;
     int32_t *hmeta;

@@ -274,14 +274,13 @@ HSTU_HD TileList make_tile_list(int32_t ctx, bool any_valid_row, int32_t band_lo
 // up to kHeavyMaxSplits contiguous chunks of its list, each processed by a work-
 // group of its own, so that no single work-group walks a whole long history (the
 // q-tile holding a sequence's min-full and target rows under a local window, the
-// last q-tiles of a long causal sequence).  A chunk holds at least 256 keys'
-// worth of tiles; a q-tile of at most that many tiles is not cut.
+// last q-tiles of a long causal sequence).  A chunk holds at least chunk_tiles
+// tiles (by default 256 keys' worth); a q-tile of at most that many is not cut.
 constexpr int32_t kHeavyMaxSplits = 4;
 HSTU_HD int32_t heavy_chunk_tiles(int32_t BN) { return BN >= 256 ? 1 : 256 / BN; }
-HSTU_HD int32_t heavy_splits(int32_t ntiles, int32_t BN) {
-    const int32_t t = heavy_chunk_tiles(BN);
-    if (ntiles <= t) return 1;
-    return imin(kHeavyMaxSplits, (ntiles + t - 1) / t);
+HSTU_HD int32_t heavy_splits(int32_t ntiles, int32_t chunk_tiles) {
+    if (ntiles <= chunk_tiles) return 1;
+    return imin(kHeavyMaxSplits, (ntiles + chunk_tiles - 1) / chunk_tiles);
 }
 // Positions [n_begin, n_end) of chunk sp of a list of ntiles tiles cut into nsp
 // chunks whose sizes differ by at most one (earlier chunks the larger).
@@ -319,17 +318,16 @@ struct WorkItem {
 HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
     WorkItem it;
     int64_t bh, rest;
-    if (p.heavy) {
-        // chunk-major: every q-tile's first chunk (the whole q-tile when it is not
-        // cut) comes first, in the schedule-2 order, then the second chunks, ...,
-        // so that the work-groups of chunks a q-tile does not have (most of them)
-        // come after all first chunks
-        const int64_t per_sp = (int64_t)p.bh_pad * p.num_qt;
-        it.sp = (int32_t)(w / per_sp);
-        const int64_t v = w % per_sp;
-        const int64_t xcd = v % 8, loc = v / 8;
-        bh = (loc / p.num_qt) * 8 + xcd;
-        it.qt = p.num_qt - 1 - (int32_t)(loc % p.num_qt);
+    if (p.levels) {
+        // q-tile levels (qt holds the level; plan_block turns it into the q-tile
+        // counted from the end of the sequence), then chunks (heavy), then
+        // (b, h): the last q-tile of every sequence, the heaviest under a causal
+        // mask (the min-full and target rows), with all its chunks first;
+        // bh % 8 = w % 8 keeps each (b, h) on one XCD
+        const int64_t per_sp = p.bh_pad, per_level = per_sp * p.num_splits;
+        it.qt = (int32_t)(w / per_level);
+        it.sp = (int32_t)((w % per_level) / per_sp);
+        bh = w % per_sp;
         it.b = (int32_t)(bh / p.H);
         it.h = (int32_t)(bh % p.H);
         it.valid = bh < (int64_t)p.B * p.H;
