@@ -360,10 +360,11 @@ def layer_main(args, torch):
 def schedule_run(w, splits, schedule):
     """The work order the library picks for schedule 0 (its rule: the persistent
     grid, 3, from 2048 possible items when the workspace holds the queues, which
-    the binding provides; else the per-item grid, 2, with the heavy q-tiles cut
-    into chunks, "2+chunks", when an unsplit grid holds fewer work-groups than
-    the chip runs at once (256 CUs, two per CU, one for hdim 256) and a sequence
-    has more than 256 keys (hdim 256: more than 8 key tiles of 32))."""
+    the binding provides; else the per-item grid, 2, unsplit in q-tile levels
+    from each sequence's end, and with each sequence's last two q-tiles cut into
+    2 to 4 chunks when that grid (at least one chunk slot more per cut q-tile)
+    holds fewer work-groups than the chip runs at once (256 CUs, two per CU, one
+    for hdim 256) and a sequence has more than 256 keys)."""
     if schedule != 0:
         return schedule
     bh_pad = (w.batch * w.nhead + 7) // 8 * 8
@@ -374,9 +375,10 @@ def schedule_run(w, splits, schedule):
     chunk = 1 if bn >= 256 else 256 // bn
     kv = w.max_seqlen_kv if w.cross else w.max_seqlen_q
     slots = 256 * (1 if w.hdim_qk >= 256 else 2)
-    if splits == 1 and items < slots and (kv + bn - 1) // bn > chunk:
-        return "2+chunks"
-    return 2
+    nq = (w.max_seqlen_q + 127) // 128
+    if splits == 1 and bh_pad * (nq + min(nq, 2)) < slots and (kv + bn - 1) // bn > chunk:
+        return "2 (levels, last q-tiles cut)"
+    return "2 (levels)" if splits == 1 else 2
 
 
 def main():

@@ -189,30 +189,50 @@ constexpr int64_t kPersistentItems = 2048;
 
 // Heavy q-tiles.  When the per-item grid of an unsplit call (schedule left to
 // the library) holds fewer work-groups than the chip runs at once, the kernel's
-// time is that of its heaviest q-tile; the q-tiles with more than a chunk of key
-// tiles (heavy_tiles_for) are then cut into chunks that run side by side, and
-// a combine pass adds the chunks' partials up.  The workspace holds the partials
-// (kHeavyMaxSplits per q-tile) and each q-tile's record, after the rest.
+// time is that of its heaviest q-tile, under a causal mask one of a sequence's
+// last (its min-full and target rows see the whole history; they may straddle
+// two q-tiles).  The last kHeavyLevels q-tiles of every sequence, when their
+// lists have more than a chunk of key tiles (heavy_tiles_for), are then cut into
+// chunks that run side by side, and a combine pass adds the chunks' partials up.
+// The chunk count is the largest (at most kHeavyMaxSplits) whose grid still fits
+// the chip at once.  The workspace holds the partials (chunk count x cut levels
+// per (b, h)) and each cut q-tile's record, after the rest.
 constexpr size_t kHeavyMaxBytes = (size_t)512 << 20;
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 size_t base_workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     return partial_bytes(a, num_splits) + (wants_queue(a) ? queue_bytes(a, num_splits) : 0);
 }
 int32_t heavy_tiles_for(const hstu_fwd_args_t *a) { return hstu::heavy_chunk_tiles(hstu::key_tile_for(a->hdim_qk)); }
-size_t heavy_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
-    if (a->schedule != 0 || num_splits != 1) return 0;
+// The cut (levels, chunk count) of a call, and the bytes of its partials and
+// records; false when nothing is cut.
+struct HeavyPlan {
+    int32_t levels, splits;
+    size_t o_bytes, lse_bytes, meta_bytes;
+};
+bool heavy_plan(const hstu_fwd_args_t *a, int32_t num_splits, HeavyPlan &h) {
+    if (a->schedule != 0 || num_splits != 1) return false;
     hstu::KernelParams p;
     fill_params(a, 1, p);
-    const int64_t items = hstu::grid_size(p);
-    if (items >= kPersistentItems || items >= (int64_t)hstu::kChipCUs * hstu::groups_per_cu_for(a->hdim_qk))
-        return 0;
+    if (hstu::grid_size(p) >= kPersistentItems) return false;  // the persistent schedule runs
     const int32_t bn = hstu::key_tile_for(a->hdim_qk);
-    if ((p.seqlen_kv + bn - 1) / bn <= heavy_tiles_for(a)) return 0;  // no q-tile is cut
-    const size_t qtiles = (size_t)items;
-    const size_t rows = qtiles * hstu::kHeavyMaxSplits * (size_t)hstu::block_m_for(a->hdim_qk);
-    const size_t b = align256(rows * (size_t)a->hdim_v * sizeof(float)) +
-                     (a->softmax ? align256(rows * sizeof(float)) : 0) + align256(qtiles * 2 * sizeof(int32_t));
-    return b <= kHeavyMaxBytes ? b : 0;
+    if ((p.seqlen_kv + bn - 1) / bn <= heavy_tiles_for(a)) return false;  // no list is long enough
+    const int64_t slots = (int64_t)hstu::kChipCUs * hstu::groups_per_cu_for(a->hdim_qk);
+    p.heavy = p.num_qt < hstu::kHeavyLevels ? p.num_qt : hstu::kHeavyLevels;
+    for (p.num_splits = hstu::kHeavyMaxSplits; p.num_splits >= 2; --p.num_splits)
+        if (hstu::grid_size(p) < slots) break;
+    if (p.heavy < 1 || p.num_splits < 2) return false;
+    const size_t qtiles = (size_t)p.bh_pad * (size_t)p.heavy;
+    const size_t rows = qtiles * (size_t)p.num_splits * (size_t)hstu::block_m_for(a->hdim_qk);
+    h.levels = p.heavy;
+    h.splits = p.num_splits;
+    h.o_bytes = align256(rows * (size_t)a->hdim_v * sizeof(float));
+    h.lse_bytes = a->softmax ? align256(rows * sizeof(float)) : 0;
+    h.meta_bytes = align256(qtiles * 2 * sizeof(int32_t));
+    return h.o_bytes + h.lse_bytes + h.meta_bytes <= kHeavyMaxBytes;
+}
+size_t heavy_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
+    HeavyPlan h;
+    return heavy_plan(a, num_splits, h) ? h.o_bytes + h.lse_bytes + h.meta_bytes : 0;
 }
 size_t workspace_bytes(const hstu_fwd_args_t *a, int32_t num_splits) {
     const size_t base = base_workspace_bytes(a, num_splits);
@@ -298,20 +318,17 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
     if (args->schedule == 0 && p.queue == nullptr && hstu::grid_size(p) < kPersistentItems) p.levels = 1;
     // heavy q-tiles cut into chunks when the per-item grid runs and the workspace
     // holds the chunks' partials (hstu_fwd_workspace_size counts them)
-    const size_t heavy = heavy_bytes(args, 1);
-    if (heavy && p.queue == nullptr && ws != nullptr && aligned16(ws) && ws_bytes >= workspace_bytes(args, 1)) {
+    HeavyPlan hp;
+    if (p.levels && heavy_plan(args, 1, hp) && ws != nullptr && aligned16(ws) &&
+        ws_bytes >= workspace_bytes(args, 1)) {
         char *h = (char *)ws + align256(base_workspace_bytes(args, 1));
-        const size_t qtiles = (size_t)p.bh_pad * (size_t)p.num_qt;
-        const size_t rows = qtiles * hstu::kHeavyMaxSplits * (size_t)hstu::block_m_for(args->hdim_qk);
-        p.heavy = 1;
+        p.heavy = hp.levels;
         p.heavy_tiles = heavy_tiles_for(args);
-        p.num_splits = hstu::kHeavyMaxSplits;
+        p.num_splits = hp.splits;
         p.hpart_o = (float *)h;
-        h += align256(rows * (size_t)args->hdim_v * sizeof(float));
-        if (args->softmax) {
-            p.hpart_lse = (float *)h;
-            h += align256(rows * sizeof(float));
-        }
+        h += hp.o_bytes;
+        if (args->softmax) p.hpart_lse = (float *)h;
+        h += hp.lse_bytes;
         p.hmeta = (int32_t *)h;
         if ((st = check_grid(p)) != HSTU_OK) return st;
     }

@@ -621,12 +621,14 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
         BlockPlan bp;
         const bool planned = plan_block<BN, NW>(p, SPLIT, bp, item);
         // heavy q-tiles: the chunk of this item (hslot >= 0 when the q-tile is cut);
-        // the first chunk's work-group records the q-tile for the combine pass
+        // the first chunk's work-group records the q-tile for the combine pass.
+        // Only the first p.heavy levels (item.qt before plan_block turned it into
+        // the q-tile) are cut.
         int32_t hslot = -1;
-        if (!SPLIT && p.heavy) {
-            const int64_t hq = ((int64_t)item.b * p.H + item.h) * p.num_qt + bp.it.qt;
+        if (!SPLIT && item.qt < p.heavy) {
+            const int64_t hq = ((int64_t)item.b * p.H + item.h) * p.heavy + item.qt;
             int32_t nsp = 0;
-            if (planned) nsp = heavy_splits(bp.tiles.count(), p.heavy_tiles);
+            if (planned) nsp = heavy_splits(bp.tiles.count(), p.heavy_tiles, p.num_splits);
             if (item.valid && item.sp == 0 && threadIdx.x == 0) {
                 const int32_t r0 = bp.it.qt * C::BM;
                 const int32_t rows = planned ? imin(C::BM, bp.s.S_q - r0) : 0;
@@ -1235,9 +1237,9 @@ constexpr int kHeavyCombineBlocks = 8;
 template <int DT, bool SOFTMAX, int BM>
 __global__ __launch_bounds__(256) void hstu_heavy_combine_kernel(KernelParams p, int D) {
     using E = Elem<DT>;
-    const int64_t hq = blockIdx.x / kHeavyCombineBlocks;
+    const int64_t hq = blockIdx.x / kHeavyCombineBlocks;  // (b, h) and level
     const int part = blockIdx.x % kHeavyCombineBlocks;
-    const int64_t bh = hq / p.num_qt;
+    const int64_t bh = hq / p.heavy;
     if (bh >= (int64_t)p.B * p.H) return;
     const int32_t meta = p.hmeta[2 * hq], tok0 = p.hmeta[2 * hq + 1];
     const int nsp = meta & 255, rows = meta >> 8;
@@ -1596,7 +1598,7 @@ hipError_t launch_combine(const KernelParams &p, int dtype, int D, bool softmax,
 }
 
 hipError_t launch_heavy_combine(const KernelParams &p, int dtype, int D, int DV, bool softmax, hipStream_t stream) {
-    const int64_t blocks = (int64_t)p.bh_pad * p.num_qt * kHeavyCombineBlocks;
+    const int64_t blocks = (int64_t)p.bh_pad * p.heavy * kHeavyCombineBlocks;
     if (blocks <= 0) return hipSuccess;
     const int bm = block_m_for(D);
     if (bm != 128) return hipErrorInvalidValue;

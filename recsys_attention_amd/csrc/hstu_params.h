@@ -47,13 +47,14 @@ struct KernelParams {
     // counted from each sequence's end (decode_work), so that the last q-tile of
     // every sequence, the heaviest under a causal mask, is dispatched first
     int32_t levels;
-    // heavy q-tiles (with levels): when set, num_splits is the largest chunk
-    // count and the split index of a work item picks its chunk of a q-tile's
-    // key-tile list, cut into chunks of at least heavy_tiles tiles; the chunks'
-    // fp32 partial results (and LSEs) go to hpart_o [slot][BM rows][Dv] and
-    // hpart_lse [slot][BM rows], slot = ((b H + h) num_qt + qt) num_splits +
-    // chunk; hmeta [(b H + h) num_qt + qt][2] holds the q-tile's chunk count |
-    // valid rows << 8 and its first token
+    // heavy q-tiles (with levels): heavy > 0 levels from each sequence's end are
+    // cut; num_splits is the largest chunk count, and the split index of a work
+    // item of those levels picks its chunk of the q-tile's key-tile list, cut
+    // into chunks of at least heavy_tiles tiles; the chunks' fp32 partial
+    // results (and LSEs) go to hpart_o [slot][BM rows][Dv] and hpart_lse
+    // [slot][BM rows], slot = hq num_splits + chunk, hq = (b H + h) heavy +
+    // level; hmeta [hq][2] holds that q-tile's chunk count | valid rows << 8 and
+    // its first token
     int32_t heavy;
     int32_t heavy_tiles;
     float *hpart_o;

@@ -270,17 +270,19 @@ HSTU_HD TileList make_tile_list(int32_t ctx, bool any_valid_row, int32_t band_lo
     return t;
 }
 
-// Heavy q-tiles (per-item grid): a q-tile whose key-tile list is long is cut into
-// up to kHeavyMaxSplits contiguous chunks of its list, each processed by a work-
-// group of its own, so that no single work-group walks a whole long history (the
-// q-tile holding a sequence's min-full and target rows under a local window, the
-// last q-tiles of a long causal sequence).  A chunk holds at least chunk_tiles
-// tiles (by default 256 keys' worth); a q-tile of at most that many is not cut.
+// Heavy q-tiles (per-item grid): the last kHeavyLevels q-tiles of a sequence,
+// whose key-tile lists are long (they hold the min-full and target rows, which
+// see the whole history, also when those rows straddle a q-tile boundary), are
+// cut into up to kHeavyMaxSplits contiguous chunks of their lists, each processed
+// by a work-group of its own, so that no single work-group walks the whole
+// history.  A chunk holds at least chunk_tiles tiles (by default 256 keys'
+// worth); a list of at most that many is not cut.
 constexpr int32_t kHeavyMaxSplits = 4;
+constexpr int32_t kHeavyLevels = 2;
 HSTU_HD int32_t heavy_chunk_tiles(int32_t BN) { return BN >= 256 ? 1 : 256 / BN; }
-HSTU_HD int32_t heavy_splits(int32_t ntiles, int32_t chunk_tiles) {
+HSTU_HD int32_t heavy_splits(int32_t ntiles, int32_t chunk_tiles, int32_t max_splits) {
     if (ntiles <= chunk_tiles) return 1;
-    return imin(kHeavyMaxSplits, (ntiles + chunk_tiles - 1) / chunk_tiles);
+    return imin(max_splits, (ntiles + chunk_tiles - 1) / chunk_tiles);
 }
 // Positions [n_begin, n_end) of chunk sp of a list of ntiles tiles cut into nsp
 // chunks whose sizes differ by at most one (earlier chunks the larger).
@@ -320,14 +322,20 @@ HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
     int64_t bh, rest;
     if (p.levels) {
         // q-tile levels (qt holds the level; plan_block turns it into the q-tile
-        // counted from the end of the sequence), then chunks (heavy), then
-        // (b, h): the last q-tile of every sequence, the heaviest under a causal
-        // mask (the min-full and target rows), with all its chunks first;
-        // bh % 8 = w % 8 keeps each (b, h) on one XCD
-        const int64_t per_sp = p.bh_pad, per_level = per_sp * p.num_splits;
-        it.qt = (int32_t)(w / per_level);
-        it.sp = (int32_t)((w % per_level) / per_sp);
-        bh = w % per_sp;
+        // counted from the end of the sequence), then (b, h): the last q-tiles of
+        // every sequence, the heaviest under a causal mask (the min-full and
+        // target rows see the whole history), first.  heavy: the first p.heavy
+        // levels come with num_splits chunk slots each (level, chunk, (b, h)),
+        // the other levels with one; bh % 8 = w % 8 keeps each (b, h) on one XCD
+        const int64_t per_hl = (int64_t)p.bh_pad * p.num_splits, hl = (int64_t)p.heavy * per_hl;
+        if (w < hl) {
+            it.qt = (int32_t)(w / per_hl);
+            it.sp = (int32_t)((w % per_hl) / p.bh_pad);
+        } else {
+            it.qt = p.heavy + (int32_t)((w - hl) / p.bh_pad);
+            it.sp = 0;
+        }
+        bh = w % p.bh_pad;
         it.b = (int32_t)(bh / p.H);
         it.h = (int32_t)(bh % p.H);
         it.valid = bh < (int64_t)p.B * p.H;
@@ -351,6 +359,8 @@ HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
 }
 
 HSTU_HD int64_t grid_size(const KernelParams &p) {
+    // heavy: num_splits chunk slots for each of the first p.heavy levels
+    if (p.heavy) return (int64_t)p.bh_pad * (p.num_qt + (int64_t)p.heavy * (p.num_splits - 1));
     return (int64_t)p.bh_pad * p.num_qt * p.num_splits;
 }
 

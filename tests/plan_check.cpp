@@ -177,10 +177,11 @@ void check_case(const Case &c) {
             // heavy q-tile chunks: sub-lists of consecutive positions that
             // concatenate to the list, at most kHeavyMaxSplits of them, none
             // empty, none cut from a list of at most chunk_tiles tiles
-            for (int chunk_tiles : {1, 2, 3, 4, 8}) {
+            for (int chunk_tiles : {1, 2, 3, 4, 8})
+            for (int max_splits = 2; max_splits <= kHeavyMaxSplits; ++max_splits) {
                 const int cnt = tl.count();
-                const int nsp = heavy_splits(cnt, chunk_tiles);
-                if (nsp < 1 || nsp > kHeavyMaxSplits || (nsp > 1 && cnt <= chunk_tiles))
+                const int nsp = heavy_splits(cnt, chunk_tiles, max_splits);
+                if (nsp < 1 || nsp > max_splits || (nsp > 1 && cnt <= chunk_tiles))
                     fail("heavy split count", cnt, nsp, chunk_tiles);
                 int expect = 0;
                 for (int sp = 0; sp < nsp; ++sp) {

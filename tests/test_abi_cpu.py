@@ -115,19 +115,22 @@ def test_workspace_size_and_checks(lib):
     # schedule left to the library: room for the persistent schedule's queues
     # (a 256-byte header and 8 bytes per possible item: 40 (b, h) pairs, 7 q-tiles
     # of 128 rows for 881 rows, times the splits); an unsplit call on a grid too
-    # small for the persistent schedule also gets the heavy q-tiles' chunk
-    # partials (4 chunks of 128 rows per q-tile, 128 fp32 columns plus an LSE)
-    # and the q-tiles' records (8 bytes each)
+    # small for the persistent schedule also gets room for cutting each
+    # sequence's last two q-tiles (3 chunks: 40 x (7 + 2 x 2) = 440 work-groups
+    # fit the chip's 512, 4 would not; 128 rows each, 128 fp32 columns plus an
+    # LSE) and the cut q-tiles' records (8 bytes each)
     queue = 256 + 8 * 40 * 7
-    slots_rows = 40 * 7 * 4 * 128
-    heavy = slots_rows * 128 * 4 + slots_rows * 4 + (40 * 7 * 8 + 255) // 256 * 256
+    slots_rows = 40 * 2 * 3 * 128
+    meta = (40 * 2 * 8 + 255) // 256 * 256
+    heavy = slots_rows * 128 * 4 + slots_rows * 4 + meta
     assert lib.hstu_fwd_workspace_size(ctypes.byref(a), 1) == (queue + 255) // 256 * 256 + heavy
     silu = _args(softmax=0)
     assert lib.hstu_fwd_workspace_size(ctypes.byref(silu), 1) == \
-        (queue + 255) // 256 * 256 + slots_rows * 128 * 4 + (40 * 7 * 8 + 255) // 256 * 256
+        (queue + 255) // 256 * 256 + slots_rows * 128 * 4 + meta
     # no room for chunks where none is cut: sequences of at most 4 key tiles
-    # (256 keys), a grid that fills the chip (hdim 256: one work-group per CU,
-    # 280 q-tiles), or an explicit schedule
+    # (256 keys), a grid that would fill the chip (hdim 256: one work-group per
+    # CU, 40 x (7 + 2) = 360 work-groups with the fewest chunk slots), or an
+    # explicit schedule
     short = _args(seqlen_q=256, seqlen_kv=256, total_q=2560)
     assert lib.hstu_fwd_workspace_size(ctypes.byref(short), 1) == 256 + 8 * 40 * 2
     wide = _args(hdim_qk=256, hdim_v=256)
@@ -262,7 +265,7 @@ def test_layer_workspace_size(lib):
     att = (n * H * d * 2 + 255) // 256 * 256
     # the attention's workspace: its work queues, and (a grid too small for the
     # persistent schedule) the heavy q-tiles' chunk partials and records
-    queue = (256 + 8 * 40 * 7 + 255) // 256 * 256 + 40 * 7 * 4 * 128 * 128 * 4 + (40 * 7 * 8 + 255) // 256 * 256
+    queue = (256 + 8 * 40 * 7 + 255) // 256 * 256 + 40 * 2 * 3 * 128 * 128 * 4 + (40 * 2 * 8 + 255) // 256 * 256
     assert lib.hstu_layer_workspace_size(ctypes.byref(a)) == proj + att + queue
     assert lib.hstu_layer_fwd(ctypes.byref(a), None, 0, None) == _abi.HSTU_ERR_WORKSPACE
     assert lib.hstu_layer_fwd(ctypes.byref(a), ctypes.c_void_p(0x700000), proj + att + queue - 1,
