@@ -130,6 +130,9 @@ def parse():
                     help="after the --warmup steps, keep warming up until this many seconds "
                          "of back-to-back launches have passed (clock ramp)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--launch", choices=("prepared", "binding"), default="prepared",
+                    help="prepared: hstu.prepare() once, then one C call per step; binding: "
+                         "the full hstu_fwd binding (checks, allocations) every step")
     ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
     ap.add_argument("--rab", choices=("none", "pos", "time", "both"), default="none",
@@ -414,10 +417,17 @@ def main():
     pairs = dev.count_pairs(schedule=args.schedule)
     flops = pairs * 2.0 * (w.hdim_qk + w.hdim_v)
 
-    def step():
-        return dev.forward(num_splits=splits, schedule=args.schedule)
+    if args.launch == "prepared":
+        # the argument block, output and workspace fixed once: each step is one C
+        # call (the binding's own per-call checks and allocations cost ~20 us of
+        # host time, more than the small workloads' kernels)
+        step = dev.prepare(num_splits=splits, schedule=args.schedule)
+    else:
+        def step():
+            return dev.forward(num_splits=splits, schedule=args.schedule)
 
     ms, timing = timed_steps(torch, step, args.steps, args.warmup, args.warmup_s, stream)
+    timing["launch"] = args.launch
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 

@@ -27,7 +27,7 @@ import torch
 from . import _abi
 
 __all__ = ["HstuGroup", "hstu_fwd", "hstu_fwd_splitkv", "hstu_fwd_splitkv_noalloc",
-           "hstu_count_visible_pairs",
+           "hstu_count_visible_pairs", "prepare", "PreparedCall",
            "workspace_size", "group_max_uih", "is_available", "library_path",
            "hstu_linear", "hstu_norm_gate", "hstu_layer", "hstu_layer_workspace_size"]
 
@@ -296,6 +296,58 @@ def hstu_fwd_splitkv_noalloc(q, k, v, num_splits, *, out, lse_out=None, stream=N
     c = _Call(q, k, v, lse_out=lse_out, **d)
     _abi.check(lib.hstu_fwd_splitkv_noalloc(ctypes.byref(c.args), int(num_splits), c.stream(stream)))
     return _result(c, d["return_lse"])
+
+
+class PreparedCall:
+    """One forward call with its argument block, output (and LSE) and workspace
+    fixed once, for loops that launch the same call again and again (serving,
+    benchmarking): each call() is one C call, hstu_fwd (num_splits == 1) or
+    hstu_fwd_splitkv, on the given or current stream, with none of the argument
+    checks and allocations of hstu_fwd.  Every call overwrites the same out (and
+    lse) and reuses the workspace, so calls must not overlap in time; the tensors
+    given to prepare() must stay alive and unchanged in shape while it is used."""
+
+    def __init__(self, lib, c, num_splits, workspace, return_lse):
+        self._lib, self._c, self._splits = lib, c, int(num_splits)
+        self._args = ctypes.byref(c.args)
+        self._ws = workspace
+        self._ws_ptr = ctypes.c_void_p(_ptr(workspace)) if workspace is not None else None
+        self._ws_bytes = workspace.numel() if workspace is not None else 0
+        self.out, self.lse = c.out, c.lse
+        self._return_lse = return_lse
+        self._streams = {}
+
+    def __call__(self, stream=None):
+        if stream is None:
+            stream = torch.cuda.current_stream(self._c.device)
+        sp = self._streams.get(stream.cuda_stream)
+        if sp is None:
+            sp = self._streams[stream.cuda_stream] = ctypes.c_void_p(stream.cuda_stream)
+        if self._splits == 1:
+            st = self._lib.hstu_fwd(self._args, self._ws_ptr, self._ws_bytes, sp)
+        else:
+            st = self._lib.hstu_fwd_splitkv(self._args, self._splits, self._ws_ptr, self._ws_bytes, sp)
+        if st != _abi.HSTU_OK:
+            _abi.check(st)
+        return (self.out, self.lse) if self._return_lse else self.out
+
+
+def prepare(q, k, v, num_splits=1, *, workspace=None, stream=None, **kw):
+    """A PreparedCall of hstu_fwd (num_splits == 1) or hstu_fwd_splitkv with these
+    arguments: checked once here (the library validates the argument block), its
+    output, LSE and workspace allocated once (on the given or current stream)."""
+    lib = _abi.load()
+    d = _call_kw(kw)
+    with _on(stream):
+        c = _Call(q, k, v, **d)
+        _abi.check(lib.hstu_validate_args(ctypes.byref(c.args)))
+        need = int(lib.hstu_fwd_workspace_size(ctypes.byref(c.args), int(num_splits)))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_cuda
+                                      or workspace.numel() < need):
+            raise ValueError(f"workspace must be a uint8 device tensor of at least {need} bytes")
+    return PreparedCall(lib, c, num_splits, workspace, d["return_lse"])
 
 
 def hstu_count_visible_pairs(q, k, v, *, stream=None, **kw) -> int:

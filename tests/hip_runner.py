@@ -63,6 +63,12 @@ class DeviceInputs:
         return hip.hstu_fwd_splitkv(self.q, self.k, self.v, num_splits, return_lse=rl,
                                     schedule=schedule, out=out, workspace=workspace, **kw)
 
+    def prepare(self, num_splits=1, schedule=0, return_lse=None):
+        """The same call as forward(), argument block and buffers fixed once."""
+        rl = self.w.softmax if return_lse is None else return_lse
+        return hip.prepare(self.q, self.k, self.v, num_splits, return_lse=rl, schedule=schedule,
+                           **self.kw)
+
     def count_pairs(self, schedule=0):
         return hip.hstu_count_visible_pairs(self.q, self.k, self.v, schedule=schedule, **self.kw)
 

@@ -356,3 +356,29 @@ def test_heavy_qtiles_cut_into_chunks(case):
     compare(oa, ob, w.dtype, "cut vs uncut")
     if softmax:
         compare_lse(lse_tokens(w, a[1]), lse_tokens(w, b[1]), "cut vs uncut")
+
+
+@pytest.mark.parametrize("name", ["batched_silu_fp16_d64", "jagged_silu_bf16_d128_local",
+                                  "group4_silu_bf16_d256", "cross_softmax_lse_splitkv16_bf16_d128"])
+def test_prepared_call_matches_binding(name):
+    """hstu.prepare(): the argument block, output and workspace fixed once; every
+    call (three in a row, then one on a side stream) gives bit for bit the output
+    (and LSE) of the full binding call."""
+    w = W.config(name)
+    _log(f"case {name}: prepared call")
+    dev = DeviceInputs(w)
+    ref = dev.forward(num_splits=w.num_splits)
+    pc = dev.prepare(num_splits=w.num_splits)
+    side = torch.cuda.Stream()
+    for i in range(4):
+        if i == 3:
+            side.wait_stream(torch.cuda.current_stream())
+            got = pc(side)
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            got = pc()
+        torch.cuda.synchronize()
+        if w.softmax:
+            assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), i
+        else:
+            assert torch.equal(got, ref), i
