@@ -182,6 +182,11 @@ __device__ __forceinline__ void silu_block(f32x16_t &x, float neg_alpha_log2e, c
     }
 }
 
+// Online softmax: the reference maximum of a row moves only when a tile's maximum
+// exceeds it by more than this (log2 units); exponents stay below 2^8, far from
+// fp32's and bf16's ranges.
+constexpr float kLazyRescale = 8.0f;
+
 // Softmax scores of one block in the log2 domain, -inf outside the visible keys.
 template <bool MASK>
 __device__ __forceinline__ float scale_block(f32x16_t &x, float sc, const RowSpan &span, int key0) {
@@ -877,15 +882,20 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                             mx = fmaxf(mx, scale_block<false>(sacc[kb], sc_soft, span, 0));
                     }
                     mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    const float m_new = fmaxf(m_run, mx);
-                    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-                    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-                    if (__ballot(corr != 1.0f) != 0) {
+                    // lazy rescale: the row's reference maximum m_run moves (and O and
+                    // l are rescaled to it) only when the tile's maximum exceeds it by
+                    // more than kLazyRescale (log2 units), so every exponent stays at
+                    // most 2^kLazyRescale; the result is the same up to rounding, and
+                    // the rescale runs a few times per row instead of on most tiles
+                    const bool raise = mx > m_run + kLazyRescale;  // m_run = -inf: any finite max
+                    if (__ballot(raise) != 0) {
+                        const float corr = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
                         l_run *= corr;
 #pragma unroll
                         for (int nb = 0; nb < C::NDB; ++nb) oacc[nb] *= corr;
+                        m_run = raise ? mx : m_run;
                     }
-                    m_run = m_new;
+                    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
                     float lsum = 0.f;
 #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb) {
