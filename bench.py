@@ -374,7 +374,7 @@ def schedule_run(w, splits, schedule):
     items = bh_pad * ((w.max_seqlen_q + 127) // 128) * splits
     if items >= 2048:
         return 3
-    bn = 128 if w.hdim_qk <= 64 else (64 if w.hdim_qk <= 128 else 32)
+    bn = 128 if w.hdim_qk <= 64 else 64
     chunk = 1 if bn >= 256 else 256 // bn
     kv = w.max_seqlen_kv if w.cross else w.max_seqlen_q
     slots = 256 * (1 if w.hdim_qk >= 256 else 2)

@@ -8,8 +8,10 @@
 namespace hstu {
 
 // The kernels' tiling per head dim: key-tile width, waves per work-group (32
-// query rows each) and so query rows per work-group.
-constexpr int key_tile_for(int D) { return D <= 64 ? 128 : (D <= 128 ? 64 : 32); }
+// query rows each) and so query rows per work-group.  hdim 256 runs one
+// work-group per CU (its registers), so its 64-key stages (64 KB each) cost no
+// occupancy, and the tile's fixed costs (barrier, wait) are halved against 32 keys.
+constexpr int key_tile_for(int D) { return D <= 64 ? 128 : 64; }
 // Four waves (128 rows): two work-groups then share a CU; eight-wave work-groups
 // (one per CU) halve the key/value traffic into LDS per row but measured slower,
 // since the CU-wide barrier keeps the two waves of each SIMD in the same phase.

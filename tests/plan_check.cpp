@@ -49,7 +49,7 @@ struct TileCfg {
     int BM, BN;
 };
 // tiny tiles to exercise the tiling logic at sizes the sweep can enumerate, and
-// the kernels' own (128 query rows; 128, 64 or 32 keys for head dims 64, 128, 256)
+// the kernels' own (128 query rows; 128 keys at head dim 64, 64 above) and 32 keys
 constexpr TileCfg kTiles[] = {{1, 1}, {2, 2}, {3, 2}, {4, 3}, {5, 8}, {8, 4}, {128, 128}, {128, 64}, {128, 32}};
 constexpr int kSplits[] = {1, 2, 3, 4, 5, 6, 16};
 
