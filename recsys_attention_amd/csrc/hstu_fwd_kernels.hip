@@ -460,38 +460,40 @@ __device__ __forceinline__ float silu_raw(float v, float neg_alpha_log2e) {
     return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * neg_alpha_log2e));
 }
 
-// One unmasked SiLU key tile of 64 keys (two 32-key blocks) for one wave at
-// hdim 128 (k_addr: 8 lane offsets, one per k-step; v_addr: 4, one per 32-column
-// block),
+// One SiLU key tile of 64 keys (two 32-key blocks) for one wave at hdim 128 or
+// 256 (k_addr: NKA lane offsets, the k-steps past them one swizzle period
+// further on; v_addr: NVA, the 32-column blocks past them 64 NVA bytes further),
 // software-pipelined so that the wave keeps the matrix pipe and the VALU busy
 // together.  Written in issue order, one step per MFMA, with scheduling fences
-// (sched_barrier) between steps so the compiler keeps the interleave:
-//   A: block 0 scores (8 MFMAs)            + block 1 K operand reads
-//   B: block 1 scores (8 MFMAs)            + block 0 SiLU (2 scores/step) + block 0 V^T reads
-//   C: block 0 P.V    (8 MFMAs)            + block 1 SiLU (2 scores/step) + block 1 V^T reads
-//   D: block 1 P.V    (8 MFMAs)
-// The next tile's global->LDS loads (issue_load(0..7)) are spread over phase A.
+// (sched_barrier) between steps so the compiler keeps the interleave (KS = D/16
+// k-steps; 2 DV/32 = KS P.V steps per block):
+//   A: block 0 scores (KS MFMAs)           + block 1 K operand reads
+//   B: block 1 scores (KS MFMAs)           + block 0 SiLU (16/KS scores/step) + block 0 V^T reads
+//   C: block 0 P.V    (KS MFMAs)           + block 1 SiLU (16/KS scores/step) + block 1 V^T reads
+//   D: block 1 P.V    (KS MFMAs)
+// The next tile's global->LDS loads (issue_load(0..KS-1)) are spread over phase A.
 // Inside each step sched_group_barrier puts the MFMA first (mask 0x008), then
 // the step's LDS reads (0x100), then its VALU work (0x002), so the matrix pipe
 // is fed before the SiLU arithmetic of the same step.
 // The fences change the instruction order only, never the arithmetic.
-template <class E, int D, class IssueLoad>
+template <class E, int D, int NKA, int NVA, class IssueLoad>
 __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const uint32_t *k_addr,
                                                     const uint32_t *v_addr, const u32x4_t *qreg,
                                                     f32x16_t *oacc, float neg_alpha_log2e,
                                                     const f32x16_t &init0, const f32x16_t &init1,
                                                     IssueLoad &&issue_load) {
     using C = Tile<D, 64>;
-    static_assert(C::NKB == 2 && C::KSTEPS == 8 && C::NDB == 4, "hdim 128, 64-key tiles");
+    constexpr int KS = C::KSTEPS, NDB = C::NDB, SPS = 16 / KS;  // SiLU scores per step
+    static_assert(C::NKB == 2 && (D == 128 || D == 256) && 2 * NDB == KS, "64-key tiles, hdim 128 or 256");
     auto kread = [&](int kb, int kk) {
-        return *(const u32x4_t *)(stage + k_addr[kk] + kb * 32 * C::RB);
+        return *(const u32x4_t *)(stage + k_addr[kk % NKA] + kb * 32 * C::RB + (kk / NKA) * (NKA * 32));
     };
-    // P.V step i of block kb: t2 = i / 4 (16-key half), nb = i % 4 (32-column block)
+    // P.V step i of block kb: t2 = i / NDB (16-key half), nb = i % NDB (32-column block)
     auto vread = [&](int kb, int i) {
-        const int t2 = i >> 2, nb = i & 3;
-        const uint8_t *va = stage + v_addr[nb] + (kb * 32 + 16 * t2) * C::RB;
+        const int t2 = i / NDB, nb = i % NDB;
+        const uint8_t *va = stage + v_addr[nb % NVA] + (kb * 32 + 16 * t2) * C::RBV + (nb / NVA) * (NVA * 64);
         const u32x2_t a0 = lds_read_tr16(va);
-        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RB);
+        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RBV);
         return u32x4_t{a0.x, a0.y, a1.x, a1.y};
     };
     auto pack8 = [&](const f32x16_t &x, int i0) {
@@ -500,17 +502,17 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     };
 
     f32x16_t s0 = init0, s1 = init1;
-    u32x4_t op0[8], op1[8];
+    u32x4_t op0[KS], op1[KS];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) op0[kk] = kread(0, kk);
+    for (int kk = 0; kk < KS; ++kk) op0[kk] = kread(0, kk);
     // Phases A-C run at wave priority 1 and the MFMA-only phase D at 0, so the
     // SIMD's other wave (another work-group, usually in a different phase) is
     // issued ahead of a wave that only feeds the matrix pipe (measured: about
     // 2 % on the long causal workload).
     __builtin_amdgcn_s_setprio(1);
-    // A (also issues the next tile's eight global->LDS loads, one per step)
+    // A (also issues the next tile's global->LDS loads, one per step)
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
         s0 = E::mfma(op0[kk], qreg[kk], s0);
         op1[kk] = kread(1, kk);
         issue_load(kk);
@@ -520,34 +522,34 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     }
     // B
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
         s1 = E::mfma(op1[kk], qreg[kk], s1);
         op0[kk] = vread(0, kk);
-        s0[2 * kk] = silu_raw(s0[2 * kk], neg_alpha_log2e);
-        s0[2 * kk + 1] = silu_raw(s0[2 * kk + 1], neg_alpha_log2e);
+#pragma unroll
+        for (int e = 0; e < SPS; ++e) s0[SPS * kk + e] = silu_raw(s0[SPS * kk + e], neg_alpha_log2e);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8 * SPS, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     const u32x4_t p0[2] = {pack8(s0, 0), pack8(s0, 8)};
     // C
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        oacc[i & 3] = E::mfma(op0[i], p0[i >> 2], oacc[i & 3]);
+    for (int i = 0; i < KS; ++i) {
+        oacc[i % NDB] = E::mfma(op0[i], p0[i / NDB], oacc[i % NDB]);
         op1[i] = vread(1, i);
-        s1[2 * i] = silu_raw(s1[2 * i], neg_alpha_log2e);
-        s1[2 * i + 1] = silu_raw(s1[2 * i + 1], neg_alpha_log2e);
+#pragma unroll
+        for (int e = 0; e < SPS; ++e) s1[SPS * i + e] = silu_raw(s1[SPS * i + e], neg_alpha_log2e);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8 * SPS, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     const u32x4_t p1[2] = {pack8(s1, 0), pack8(s1, 8)};
     // D
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) oacc[i & 3] = E::mfma(op1[i], p1[i >> 2], oacc[i & 3]);
+    for (int i = 0; i < KS; ++i) oacc[i % NDB] = E::mfma(op1[i], p1[i / NDB], oacc[i % NDB]);
 }
 
 // RAB: relative attention bias.  The bias is added to alpha q.k before the mask
@@ -935,7 +937,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
             end_step();
         };
-        if constexpr (!SOFTMAX && D == 128 && DV == 128) {
+        if constexpr (!SOFTMAX && BN == 64 && (D == 128 || D == 256) && DV == D) {
             // Every key tile runs through the software-pipelined body.  In a tile
             // that some valid row of the work-group sees only in part, the mask
             // enters the score MFMAs' initial accumulator: a hidden score starts at
@@ -948,6 +950,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
             // register set.  A wave none of whose rows sees such a tile only issues
             // its share of the next tile's loads.
             const float mask_val = copysignf(1e30f, neg_alpha_log2e);
+            static_assert(LPT <= C::KSTEPS, "phase A issues every load of the next tile");
             auto step = [&](int n, auto stage_const) {
                 constexpr int buf = decltype(stage_const)::value;
                 constexpr int nbuf = buf ^ 1;
@@ -980,7 +983,7 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                         }
                 }
                 if (wave_any) {
-                    silu_tile_pipelined<E, D>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
+                    silu_tile_pipelined<E, D, NKA, NVA>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
                                               init[0], init[1], [&](int idx) {
                                                   if (idx < LPT) issue_one(t_next, nbuf, idx);
                                               });
