@@ -552,6 +552,138 @@ __device__ __forceinline__ void silu_tile_pipelined(const uint8_t *stage, const 
     for (int i = 0; i < KS; ++i) oacc[i % NDB] = E::mfma(op1[i], p1[i / NDB], oacc[i % NDB]);
 }
 
+// One softmax key tile of 64 keys (two 32-key blocks) for one wave at hdim 128 or
+// 256, software-pipelined like silu_tile_pipelined, with the online softmax of
+// the generic body (log2 domain, lazy reference maximum m_run, sum l_run):
+//   A: block 0 scores (KS MFMAs)           + block 1 K operand reads + the next tile's loads
+//      then block 0 scaled, its row maximum, the reference raised if needed
+//   B: block 1 scores (KS MFMAs)           + block 0 exponentials + block 0 V^T reads
+//   C: block 0 P.V    (KS MFMAs)           + block 1 scaled and its maximum + block 1 V^T reads
+//      then the reference raised if needed (O, l and block 0's sum rescaled, after
+//      block 0's P.V), block 1 exponentials
+//   D: block 1 P.V    (KS MFMAs)
+// Hidden scores come in through the initial accumulators as in the SiLU body
+// (about -1e30 |alpha log2e| once scaled): their exponentials are exact zeros.
+template <class E, int D, int NKA, int NVA, class IssueLoad>
+__device__ __forceinline__ void softmax_tile_pipelined(const uint8_t *stage, const uint32_t *k_addr,
+                                                       const uint32_t *v_addr, const u32x4_t *qreg,
+                                                       f32x16_t *oacc, float sc, float &m_run, float &l_run,
+                                                       const f32x16_t &init0, const f32x16_t &init1,
+                                                       IssueLoad &&issue_load) {
+    using C = Tile<D, 64>;
+    constexpr int KS = C::KSTEPS, NDB = C::NDB, SPS = 16 / KS;
+    static_assert(C::NKB == 2 && (D == 128 || D == 256) && 2 * NDB == KS, "64-key tiles, hdim 128 or 256");
+    auto kread = [&](int kb, int kk) {
+        return *(const u32x4_t *)(stage + k_addr[kk % NKA] + kb * 32 * C::RB + (kk / NKA) * (NKA * 32));
+    };
+    auto vread = [&](int kb, int i) {
+        const int t2 = i / NDB, nb = i % NDB;
+        const uint8_t *va = stage + v_addr[nb % NVA] + (kb * 32 + 16 * t2) * C::RBV + (nb / NVA) * (NVA * 64);
+        const u32x2_t a0 = lds_read_tr16(va);
+        const u32x2_t a1 = lds_read_tr16(va + 8 * C::RBV);
+        return u32x4_t{a0.x, a0.y, a1.x, a1.y};
+    };
+    auto pack8 = [&](const f32x16_t &x, int i0) {
+        return u32x4_t{E::pack2(x[i0 + 0], x[i0 + 1]), E::pack2(x[i0 + 2], x[i0 + 3]),
+                       E::pack2(x[i0 + 4], x[i0 + 5]), E::pack2(x[i0 + 6], x[i0 + 7])};
+    };
+    // the row's maximum over both lane groups; a block without a visible key (all
+    // its scores the masking value, -1e30 |sc| once scaled) gives -inf, so that it
+    // never becomes the row's reference
+    const float no_key = -5e29f * fabsf(sc);
+    auto row_max = [&](float mx) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        return mx < no_key ? -INFINITY : mx;
+    };
+    // raise the reference to mx where it exceeds it by more than kLazyRescale:
+    // O, l (and the sum so far of this tile) rescaled to the new reference
+    auto raise_to = [&](float mx, float &lsum) {
+        const bool raise = mx > m_run + kLazyRescale;
+        if (__ballot(raise) != 0) {
+            const float corr = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+            l_run *= corr;
+            lsum *= corr;
+#pragma unroll
+            for (int nb = 0; nb < NDB; ++nb) oacc[nb] *= corr;
+            m_run = raise ? mx : m_run;
+        }
+    };
+
+    f32x16_t s0 = init0, s1 = init1;
+    u32x4_t op0[KS], op1[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) op0[kk] = kread(0, kk);
+    __builtin_amdgcn_s_setprio(1);
+    // A
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        s0 = E::mfma(op0[kk], qreg[kk], s0);
+        op1[kk] = kread(1, kk);
+        issue_load(kk);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    float lsum = 0.0f;
+    {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0[i] *= sc;
+            mx = fmaxf(mx, s0[i]);
+        }
+        raise_to(row_max(mx), lsum);
+    }
+    float m_use = m_run == -INFINITY ? 0.0f : m_run;
+    // B
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        s1 = E::mfma(op1[kk], qreg[kk], s1);
+        op0[kk] = vread(0, kk);
+#pragma unroll
+        for (int e = 0; e < SPS; ++e) {
+            const float x = __builtin_amdgcn_exp2f(s0[SPS * kk + e] - m_use);
+            lsum += x;
+            s0[SPS * kk + e] = x;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * SPS, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const u32x4_t p0[2] = {pack8(s0, 0), pack8(s0, 8)};
+    // C
+    float mx1 = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        oacc[i % NDB] = E::mfma(op0[i], p0[i / NDB], oacc[i % NDB]);
+        op1[i] = vread(1, i);
+#pragma unroll
+        for (int e = 0; e < SPS; ++e) {
+            s1[SPS * i + e] *= sc;
+            mx1 = fmaxf(mx1, s1[SPS * i + e]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * SPS, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    raise_to(row_max(mx1), lsum);
+    m_use = m_run == -INFINITY ? 0.0f : m_run;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float x = __builtin_amdgcn_exp2f(s1[i] - m_use);
+        lsum += x;
+        s1[i] = x;
+    }
+    const u32x4_t p1[2] = {pack8(s1, 0), pack8(s1, 8)};
+    // D
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) oacc[i % NDB] = E::mfma(op1[i], p1[i / NDB], oacc[i % NDB]);
+    l_run += lsum;
+}
+
 // RAB: relative attention bias.  The bias is added to alpha q.k before the mask
 // and the non-linearity; it enters as the score MFMAs' initial accumulator,
 // divided by alpha (rab_tile), so the scores, the non-linearity and the epilogue
@@ -937,14 +1069,16 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
 
             end_step();
         };
-        if constexpr (!SOFTMAX && BN == 64 && (D == 128 || D == 256) && DV == D) {
+        // (the softmax body at hdim 256 would spill: it keeps the generic body there)
+        if constexpr (BN == 64 && (D == 128 || (D == 256 && !SOFTMAX)) && DV == D) {
             // Every key tile runs through the software-pipelined body.  In a tile
             // that some valid row of the work-group sees only in part, the mask
             // enters the score MFMAs' initial accumulator: a hidden score starts at
             // mask_val = 1e30 with the sign of -alpha, so that -alpha log2e times it
             // is huge and positive, exp2 of it +inf, and SiLU of it exactly zero
-            // (with the bias, a visible score keeps its bias and a hidden one is
-            // replaced).  Building the accumulators costs two VALU instructions per
+            // (softmax: alpha log2e times it is huge and negative, its exponential
+            // exactly zero; with the bias, a visible score keeps its bias and a
+            // hidden one is replaced).  Building the accumulators costs two VALU instructions per
             // score (v_bfe_i32 of the lane's key bit, then a bitfield select), only
             // in those tiles; one body, one call site, so the loop keeps one
             // register set.  A wave none of whose rows sees such a tile only issues
@@ -983,10 +1117,15 @@ __global__ __launch_bounds__(64 * waves_for(D)) __attribute__((amdgpu_waves_per_
                         }
                 }
                 if (wave_any) {
-                    silu_tile_pipelined<E, D, NKA, NVA>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc, neg_alpha_log2e,
-                                              init[0], init[1], [&](int idx) {
-                                                  if (idx < LPT) issue_one(t_next, nbuf, idx);
-                                              });
+                    auto issue = [&](int idx) {
+                        if (idx < LPT) issue_one(t_next, nbuf, idx);
+                    };
+                    if constexpr (SOFTMAX)
+                        softmax_tile_pipelined<E, D, NKA, NVA>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc,
+                                                               sc_soft, m_run, l_run, init[0], init[1], issue);
+                    else
+                        silu_tile_pipelined<E, D, NKA, NVA>(lds0 + buf * C::STAGE, k_addr, v_addr, qreg, oacc,
+                                                            neg_alpha_log2e, init[0], init[1], issue);
                 } else {
 #pragma unroll
                     for (int idx = 0; idx < LPT; ++idx) issue_one(t_next, nbuf, idx);
