@@ -152,10 +152,11 @@ hstu_status_t hstu_validate_args(const hstu_fwd_args_t *args);
  * plus, when args->schedule is 0 or 3, the work queues (256 bytes and 8 per possible
  * item: batch * nhead rounded up to 8, times the q-tiles of max_seqlen_q in 128 rows,
  * times num_splits), plus, for an unsplit call with schedule 0 whose per-item grid
- * is smaller than the chip's resident work-groups, room for cutting long q-tiles
- * into chunks (4 fp32 partials of 128 rows per q-tile, their LSEs for softmax, and
- * 8 bytes per q-tile; at most 512 MiB, else the room is left out and nothing is
- * cut).  Host-only; returns 0 on invalid arguments. */
+ * is smaller than the chip's resident work-groups, room for cutting each
+ * sequence's last two q-tiles into 2 to 4 chunks (an fp32 partial of 128 rows per
+ * chunk, its LSEs for softmax, and an 8-byte record per cut q-tile; at most
+ * 512 MiB, else the room is left out and nothing is cut).  Host-only; returns 0 on
+ * invalid arguments. */
 size_t hstu_fwd_workspace_size(const hstu_fwd_args_t *args, int32_t num_splits);
 
 /* The forward operator: one fused kernel per call (plus, for schedule 3, an 8-work-
@@ -163,8 +164,9 @@ size_t hstu_fwd_workspace_size(const hstu_fwd_args_t *args, int32_t num_splits);
  * chunks, a combine kernel).  ws may be NULL: then schedule 0 runs as 2, and
  * schedule 3 fails with HSTU_ERR_WORKSPACE.  Schedule 0 on a small per-item grid
  * runs the q-tiles in levels from each sequence's end, and, with room in ws, cuts
- * q-tiles of more than 256 keys' worth of key tiles into up to 4 chunks whose fp32
- * partials a combine kernel adds up (same terms, another order of addition).  A workspace of at least
+ * each sequence's last two q-tiles, when longer than 256 keys' worth of key tiles,
+ * into up to 4 chunks whose fp32 partials a combine kernel adds up (same terms,
+ * another order of addition).  A workspace of at least
  * hstu_fwd_workspace_size(args, 1) bytes, 16-byte aligned, is used by schedule 0
  * and 3; its contents need no initialisation; calls that share a workspace must
  * not overlap in time. */
