@@ -189,8 +189,9 @@ hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, 
  * array of HSTU_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
  * on until the process ends.  The caller passes inputs and outputs as for
  * hstu_fwd_splitkv; the call allocates and frees nothing.  A problem whose
- * workspace (hstu_fwd_workspace_size without the room for chunks of long q-tiles,
- * which this entry point never cuts) exceeds the scratch is rejected with
+ * workspace (hstu_fwd_workspace_size without the room for cutting long q-tiles
+ * into chunks: that room is used only when the scratch holds it too) exceeds the
+ * scratch is rejected with
  * HSTU_ERR_WORKSPACE before anything runs.  All calls on one GPU share its
  * scratch (each call's kernels overwrite what they use; nothing needs to start at
  * zero): calls that overlap in time on one GPU (other streams, other threads)

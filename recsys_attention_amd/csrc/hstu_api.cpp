@@ -374,8 +374,8 @@ hstu_status_t hstu_fwd_splitkv_noalloc(const hstu_fwd_args_t *args, int32_t num_
     if (st != HSTU_OK) return st;
     if (num_splits < 1 || num_splits > HSTU_MAX_SPLITS)
         return fail(HSTU_ERR_INVALID_ARG, "num_splits %d not in 1..%d", num_splits, HSTU_MAX_SPLITS);
-    // (the heavy q-tiles' partials are left out: without room for them the
-    // q-tiles are not cut)
+    // (the room for cutting heavy q-tiles is left out: hstu_fwd cuts them only
+    // when the scratch holds that room too)
     const size_t need = base_workspace_bytes(args, num_splits);
     if (need > hstu::kScratchBytes)
         return fail(HSTU_ERR_WORKSPACE,
