@@ -127,8 +127,7 @@ __device__ __forceinline__ bool plan_block(const KernelParams &p, bool split, Bl
     if (p.levels && p.queue == nullptr) {
         // level l counted from the sequence's last q-tile: q-tile nq - 1 - l, and
         // the levels past the sequence onto the q-tiles past it (one to one)
-        const int32_t nq = (bp.s.S_q + 32 * NW - 1) / (32 * NW), l = bp.it.qt;
-        bp.it.qt = l < nq ? nq - 1 - l : l;
+        bp.it.qt = level_qtile(bp.it.qt, (bp.s.S_q + 32 * NW - 1) / (32 * NW));
     }
     const int32_t r0 = bp.it.qt * (32 * NW);
     if (r0 >= bp.s.S_q) return false;

@@ -358,6 +358,11 @@ HSTU_HD WorkItem decode_work(const KernelParams &p, int64_t w) {
     return it;
 }
 
+// Level l of a sequence with nq q-tiles (levels order): its q-tile counted from
+// the end, nq - 1 - l; the levels past the sequence map one to one onto the
+// q-tiles past its end (which hold no rows).  A bijection of [0, num_qt).
+HSTU_HD int32_t level_qtile(int32_t l, int32_t nq) { return l < nq ? nq - 1 - l : l; }
+
 HSTU_HD int64_t grid_size(const KernelParams &p) {
     // heavy: num_splits chunk slots for each of the first p.heavy levels
     if (p.heavy) return (int64_t)p.bh_pad * (p.num_qt + (int64_t)p.heavy * (p.num_splits - 1));

@@ -28,6 +28,10 @@
 //   splits          split_range cuts [0, nt) into contiguous, disjoint ranges
 //                   that cover it (1 .. 6 splits and 16), and the per-split tile
 //                   lists concatenate to the unsplit list;
+//   work order      decode_work gives each item of the grid exactly once, each
+//                   (b, h) on one XCD, for schedules 1 and 2, level order and
+//                   level order with chunk slots; levels map onto q-tiles one to
+//                   one (once, before the cases);
 //   pair count      counting as the device count kernel does (work-group test,
 //                   then row classes, then the predicate) gives the mask's
 //                   number of visible pairs.
@@ -223,9 +227,72 @@ void check_case(const Case &c) {
     }
 }
 
+// decode_work over a whole grid, for every per-item order: each item (b, h,
+// q-tile, split) of the problem exactly once, each (b, h) on one XCD (id % 8) in
+// the orders that promise it, and the levels mapping q-tiles one to one.
+void check_decode() {
+    KernelParams p;
+    std::memset(&p, 0, sizeof(p));
+    for (int B = 1; B <= 5; ++B)
+        for (int H = 1; H <= 3; ++H)
+            for (int num_qt = 1; num_qt <= 5; ++num_qt)
+                for (int mode = 0; mode < 4; ++mode)
+                    for (int S = 1; S <= 4; ++S) {
+                        const int heavy = mode == 3 ? (num_qt < 2 ? num_qt : 2) : 0;
+                        if ((mode >= 2 && mode < 3 && S > 1) || (mode == 3 && S < 2)) continue;
+                        p.B = B;
+                        p.H = H;
+                        p.bh_pad = (B * H + 7) / 8 * 8;
+                        p.num_qt = num_qt;
+                        p.num_splits = S;
+                        p.schedule = mode == 0 ? 1 : 2;
+                        p.levels = mode >= 2;
+                        p.heavy = heavy;
+                        const int64_t grid = grid_size(p);
+                        const int64_t expect = (int64_t)p.bh_pad * (heavy ? num_qt + heavy * (S - 1) : num_qt * S);
+                        if (grid != expect) fail("grid size", mode, (int)grid, (int)expect);
+                        // seen[bh][qt or level][sp]
+                        std::vector<int> seen((size_t)B * H * num_qt * S, 0);
+                        for (int64_t w = 0; w < grid; ++w) {
+                            const WorkItem it = decode_work(p, w);
+                            const int64_t bh = (int64_t)it.b * H + it.h;
+                            if (!it.valid) {
+                                if (bh < (int64_t)B * H && mode != 0 && it.qt >= 0) fail("valid item marked invalid", mode, (int)w);
+                                continue;
+                            }
+                            if (bh < 0 || bh >= (int64_t)B * H || it.qt < 0 || it.qt >= num_qt || it.sp < 0 || it.sp >= S)
+                                fail("decoded item out of range", mode, (int)w, it.qt);
+                            if (mode >= 1 && bh % 8 != w % 8) fail("(b, h) off its XCD", mode, (int)w, (int)bh);
+                            if (heavy && it.qt >= heavy && it.sp != 0) fail("chunk slot past the cut levels", (int)w, it.qt, it.sp);
+                            ++seen[((size_t)bh * num_qt + it.qt) * S + it.sp];
+                        }
+                        for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
+                            for (int q = 0; q < num_qt; ++q)
+                                for (int sp = 0; sp < S; ++sp) {
+                                    const int want = (mode == 2) ? (sp == 0) : (mode == 3 ? (q < heavy || sp == 0) : 1);
+                                    if (seen[((size_t)bh * num_qt + q) * S + sp] != want)
+                                        fail("item not decoded exactly once", mode, q, sp);
+                                }
+                    }
+    // levels onto q-tiles: a bijection of [0, num_qt) for every sequence length
+    for (int num_qt = 1; num_qt <= 9; ++num_qt)
+        for (int nq = 0; nq <= num_qt; ++nq) {
+            std::vector<int> hit(num_qt, 0);
+            for (int l = 0; l < num_qt; ++l) {
+                const int q = level_qtile(l, nq);
+                if (q < 0 || q >= num_qt) fail("level maps outside the q-tiles", l, nq, q);
+                ++hit[q];
+                if (l < nq && q != nq - 1 - l) fail("level is not counted from the end", l, nq, q);
+            }
+            for (int q = 0; q < num_qt; ++q)
+                if (hit[q] != 1) fail("levels do not map one to one", q, nq, num_qt);
+        }
+}
+
 }  // namespace
 
 int main() {
+    check_decode();
     Case c;
     while (std::scanf("%d %d %d %d %d %d %d %d", &c.S_q, &c.S_kv, &c.C, &c.T, &c.cross, &c.L, &c.M, &c.causal) == 8) {
         if (c.S_q < 0 || c.S_kv < 0 || c.S_q > 100000 || c.S_kv > 100000) fail("bad header");
