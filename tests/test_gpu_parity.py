@@ -329,24 +329,27 @@ def test_self_equals_cross_on_context_and_history_prefix(softmax, local_len, con
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(10))
 def test_heavy_qtiles_cut_into_chunks(case):
     """Unsplit calls left to the library on a grid too small for the persistent
     schedule cut each sequence's last two q-tiles, when their key-tile lists are
     long (the min-full and target rows under a local window, the tail of a causal
     sequence), into chunks on separate work-groups, combined afterwards (CK README
     "Split-KV", applied per q-tile).  Cases 6 and 7 put the min-full and target
-    rows across a q-tile boundary (1414 rows: 1402..1407 and 1408..1413).  Against
-    the oracle, and against the uncut per-item grid (schedule 2) within the same
+    rows across a q-tile boundary (1414 rows: 1402..1407 and 1408..1413); cases 8
+    and 9 are batched (every sequence 1200 events and 6 targets).  Against the
+    oracle, and against the uncut per-item grid (schedule 2) within the same
     tolerance; pair counts exact."""
     d, dv, softmax, L, M = [(128, 128, False, 5, 6), (128, 128, True, 5, 6), (256, 256, False, 0, 0),
                             (64, 64, True, 8, 16), (96, 64, False, 3, 9), (128, 128, False, 0, 0),
-                            (128, 128, False, 5, 6), (128, 128, True, 5, 6)][case]
-    uih = [1402, 700, 90] if case >= 6 else [1500, 700, 90]
+                            (128, 128, False, 5, 6), (128, 128, True, 5, 6), (128, 128, False, 5, 6),
+                            (128, 128, True, 0, 0)][case]
+    uih, tg, jagged = ([1402, 700, 90], [6, 3, 1], True) if case in (6, 7) else \
+        (([1200] * 3, [6] * 3, False) if case >= 8 else ([1500, 700, 90], [6, 3, 1], True))
     groups = [W.MaskGroup(L, 6, M, 0.0)]
     w = W.build("heavy", dtype="bf16" if case % 2 == 0 else "fp16", batch=3, nhead=2, hdim_qk=d, hdim_v=dv,
-                jagged=True, cross=False, causal=True, softmax=softmax, alpha=0.0, groups=groups,
-                uih_q=uih, targets=[6, 3, 1], seed=300 + case)
+                jagged=jagged, cross=False, causal=True, softmax=softmax, alpha=0.0, groups=groups,
+                uih_q=uih, targets=tg, seed=300 + case)
     stats = _check_full(w, schedule=0)
     dev = DeviceInputs(w)
     a, b = dev.forward(schedule=0), dev.forward(schedule=2)
