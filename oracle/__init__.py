@@ -23,6 +23,10 @@ Parity status (what pins each function, see tests/test_oracle_*.py):
   * HSTU layer (oracle/layer.py: f1 + SiLU + split, attention, norm * gate,
                     f2 + residual) - pinned by an independent torch float64
                     evaluation and the zero-gate / zero-f2 identities.
+
+Precision: the default build evaluates in double precision; load_fp32() gives
+the same C source built with ORACLE_FP32 (single precision throughout a row),
+and tests/test_oracle_fp32.py bounds the difference between the two.
 """
 from __future__ import annotations
 
@@ -36,7 +40,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hstu_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_LIB32_PATH = os.path.join(_HERE, "liboracle32.so")
 _lib = None
+_lib32 = None
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -55,6 +61,22 @@ def build(src: str = _SRC, out: str = _LIB_PATH, extra_flags=()) -> str:
            out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
+
+
+def build_fp32(out: str = _LIB32_PATH, extra_flags=()) -> str:
+    """Compile the single-precision build of the oracle."""
+    return build(out=out, extra_flags=["-DORACLE_FP32", *extra_flags])
+
+
+def load_fp32():
+    """The single-precision build (compiled first if missing or older than the source);
+    pass it as lib= to any function below."""
+    global _lib32
+    if _lib32 is None:
+        if not os.path.exists(_LIB32_PATH) or os.path.getmtime(_LIB32_PATH) < os.path.getmtime(_SRC):
+            build_fp32()
+        _lib32 = load(_LIB32_PATH)
+    return _lib32
 
 
 def load(path: Optional[str] = None):

@@ -18,7 +18,10 @@
  *                    row gives o = 0 and LSE = -inf.
  * Everything is evaluated in double precision from the fp32 values of the
  * rounded inputs, one (sequence, head, row) at a time, with the dense mask of
- * each sequence materialised first from the rule below.
+ * each sequence materialised first from the rule below.  Built with
+ * -DORACLE_FP32 the same steps run in single precision (scores, SiLU, softmax
+ * sums and the output accumulation in float, expf/logf): the fp32 oracle, whose
+ * own rounding error the double build bounds.
  *
  * The mask rule (CK README "Masking" table; readings of the points the pages
  * leave open are listed with each step).  Per sequence, with C = context_len,
@@ -56,6 +59,17 @@
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
+#endif
+
+/* arithmetic type of one row's evaluation (see the header) */
+#ifdef ORACLE_FP32
+typedef float real_t;
+#define R_EXP expf
+#define R_LOG logf
+#else
+typedef double real_t;
+#define R_EXP exp
+#define R_LOG log
 #endif
 
 /* per-sequence class boundaries of the query and key axes */
@@ -151,54 +165,58 @@ static double rab_bias(const rab_t *r, const seq_t *s, int h, int i, int j)
     return bias;
 }
 
-/* one output row: o_row[Dv] (and *lse) from the row's dense mask */
+/* one output row: o_row[Dv] (and *lse) from the row's dense mask; sbuf holds
+ * S_kv + Dv values (the row's scores, then its output accumulator) */
 static void row_forward(const seq_t *s, int h, int i, const unsigned char *mask_row,
                         int H, int Dqk, int Dv, int softmax, double alpha,
                         const float *q, const float *k, const float *v, const rab_t *rab,
-                        double *o_row, double *lse_out, double *sbuf)
+                        double *o_row, double *lse_out, real_t *sbuf)
 {
     const float *qi = q + ((s->q0 + i) * H + h) * (int64_t)Dqk;
-    for (int e = 0; e < Dv; ++e) o_row[e] = 0.0;
+    real_t *acc = sbuf + s->S_kv;
+    const real_t al = (real_t)alpha, a = (real_t)s->a;
+    for (int e = 0; e < Dv; ++e) acc[e] = 0;
     /* scores of the visible keys */
-    double smax = -INFINITY;
+    real_t smax = -INFINITY;
     int nvis = 0;
     for (int j = 0; j < s->S_kv; ++j) {
         if (!mask_row[j]) continue;
         const float *kj = k + ((s->kv0 + j) * H + h) * (int64_t)Dqk;
-        double dot = 0.0;
-        for (int e = 0; e < Dqk; ++e) dot += (double)qi[e] * (double)kj[e];
-        sbuf[j] = alpha * dot + rab_bias(rab, s, h, i, j);
+        real_t dot = 0;
+        for (int e = 0; e < Dqk; ++e) dot += (real_t)qi[e] * (real_t)kj[e];
+        sbuf[j] = al * dot + (real_t)rab_bias(rab, s, h, i, j);
         if (sbuf[j] > smax) smax = sbuf[j];
         ++nvis;
     }
     if (!softmax) {
         for (int j = 0; j < s->S_kv; ++j) {
             if (!mask_row[j]) continue;
-            double x = sbuf[j];
-            double p = x / (1.0 + exp(-x));           /* SiLU(x) = x * sigmoid(x) */
+            real_t x = sbuf[j];
+            real_t p = x / (1 + R_EXP(-x));           /* SiLU(x) = x * sigmoid(x) */
             const float *vj = v + ((s->kv0 + j) * H + h) * (int64_t)Dv;
-            for (int e = 0; e < Dv; ++e) o_row[e] += p * (double)vj[e];
+            for (int e = 0; e < Dv; ++e) acc[e] += p * (real_t)vj[e];
         }
-        for (int e = 0; e < Dv; ++e) o_row[e] *= s->a;
+        for (int e = 0; e < Dv; ++e) o_row[e] = (double)(acc[e] * a);
         if (lse_out) *lse_out = 0.0;
         return;
     }
     if (nvis == 0) {                                  /* empty row: o = 0, LSE = -inf */
+        for (int e = 0; e < Dv; ++e) o_row[e] = 0.0;
         if (lse_out) *lse_out = -INFINITY;
         return;
     }
-    double denom = 0.0;
+    real_t denom = 0;
     for (int j = 0; j < s->S_kv; ++j)
-        if (mask_row[j]) denom += exp(sbuf[j] - smax);
-    double lse = smax + log(denom);
+        if (mask_row[j]) denom += R_EXP(sbuf[j] - smax);
+    real_t lse = smax + R_LOG(denom);
     for (int j = 0; j < s->S_kv; ++j) {
         if (!mask_row[j]) continue;
-        double p = exp(sbuf[j] - lse);
+        real_t p = R_EXP(sbuf[j] - lse);
         const float *vj = v + ((s->kv0 + j) * H + h) * (int64_t)Dv;
-        for (int e = 0; e < Dv; ++e) o_row[e] += p * (double)vj[e];
+        for (int e = 0; e < Dv; ++e) acc[e] += p * (real_t)vj[e];
     }
-    for (int e = 0; e < Dv; ++e) o_row[e] *= s->a;
-    if (lse_out) *lse_out = lse;
+    for (int e = 0; e < Dv; ++e) o_row[e] = (double)(acc[e] * a);
+    if (lse_out) *lse_out = (double)lse;
 }
 
 /* shared argument bundle of the exported functions */
@@ -322,7 +340,7 @@ static int hstu_fwd_impl(const problem_t *pp, const rab_t *rab, const float *q, 
         int rows = s->S_q * H;
 #pragma omp parallel
         {
-            double *sbuf = (double *)malloc(sizeof(double) * (size_t)(s->S_kv + 1));
+            real_t *sbuf = (real_t *)malloc(sizeof(real_t) * (size_t)(s->S_kv + Dv + 1));
 #pragma omp for schedule(dynamic, 4)
             for (int r = 0; r < rows; ++r) {
                 int h = r % H, i = r / H;
@@ -390,7 +408,7 @@ static int hstu_rows_impl(const problem_t *pp, const rab_t *rab, const float *q,
     {
         int maxkv = 1;
         for (int b = 0; b < B; ++b) maxkv = imax(maxkv, seqs[b].S_kv);
-        double *sbuf = (double *)malloc(sizeof(double) * (size_t)maxkv);
+        real_t *sbuf = (real_t *)malloc(sizeof(real_t) * (size_t)(maxkv + Dv));
         unsigned char *mrow = (unsigned char *)malloc((size_t)maxkv);
 #pragma omp for schedule(dynamic, 1)
         for (int r = 0; r < n; ++r) {

@@ -25,8 +25,8 @@ MUTATIONS = {
     "minfull_off_by_one": ("u >= s->Uq - s->M", "u > s->Uq - s->M"),
     "targets_ignore_minfull": ("full = (s->L == 0) || (s->M > 0);", "full = (s->L == 0);"),
     "cross_top_left": ("x = u + (s->Ukv - s->Uq);", "x = u;"),
-    "silu_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
-    "alpha_dropped": ("sbuf[j] = alpha * dot +", "sbuf[j] = dot +"),
+    "silu_sign": ("x / (1 + R_EXP(-x))", "x / (1 + R_EXP(x))"),
+    "alpha_dropped": ("sbuf[j] = al * dot +", "sbuf[j] = dot +"),
     "rab_bucket_strict": ("if (kRabEdges[e] <= d) b = e + 1;", "if (kRabEdges[e] < d) b = e + 1;"),
     "rab_time_head_zero": ("r->time_tab[(int64_t)h * RAB_BUCKETS", "r->time_tab[(int64_t)0 * RAB_BUCKETS"),
     "rab_pos_signed": ("int d = i > j ? i - j : j - i;", "int d = i > j ? i - j : 0;"),
@@ -37,16 +37,17 @@ MUTATIONS = {
     "wrong_head_of_k": ("const float *kj = k + ((s->kv0 + j) * H + h)",
                         "const float *kj = k + ((s->kv0 + j) * H + 0)"),
     "v_row_of_query": ("const float *vj = v + ((s->kv0 + j) * H + h) * (int64_t)Dv;\n"
-                       "            for (int e = 0; e < Dv; ++e) o_row[e] += p * (double)vj[e];\n"
+                       "            for (int e = 0; e < Dv; ++e) acc[e] += p * (real_t)vj[e];\n"
                        "        }\n        for",
                        "const float *vj = v + ((s->kv0 + i) * H + h) * (int64_t)Dv;\n"
-                       "            for (int e = 0; e < Dv; ++e) o_row[e] += p * (double)vj[e];\n"
+                       "            for (int e = 0; e < Dv; ++e) acc[e] += p * (real_t)vj[e];\n"
                        "        }\n        for"),
-    "silu_attn_scale_dropped": ("        for (int e = 0; e < Dv; ++e) o_row[e] *= s->a;\n"
+    "silu_attn_scale_dropped": ("        for (int e = 0; e < Dv; ++e) o_row[e] = (double)(acc[e] * a);\n"
                                 "        if (lse_out) *lse_out = 0.0;",
+                                "        for (int e = 0; e < Dv; ++e) o_row[e] = (double)acc[e];\n"
                                 "        if (lse_out) *lse_out = 0.0;"),
-    "lse_without_max": ("double lse = smax + log(denom);", "double lse = log(denom);"),
-    "softmax_unnormalised": ("double p = exp(sbuf[j] - lse);", "double p = exp(sbuf[j] - smax);"),
+    "lse_without_max": ("real_t lse = smax + R_LOG(denom);", "real_t lse = R_LOG(denom);"),
+    "softmax_unnormalised": ("real_t p = R_EXP(sbuf[j] - lse);", "real_t p = R_EXP(sbuf[j] - smax);"),
     "group_interleaved": ("return b / (p->B / p->G);", "return b % p->G;"),
     "default_scale_physical_len": ("seqs[b].Uq > mx) mx = seqs[b].Uq;",
                                    "seqs[b].S_q > mx) mx = seqs[b].S_q;"),

@@ -1,8 +1,9 @@
 """The oracle's C code built with AddressSanitizer and UndefinedBehaviorSanitizer
 (gcc, OpenMP) and run in a child process over small problems covering every entry
 point (dense mask, whole forward, selected rows, pair counts, sequence info, the
-biased forward and rows, the bucket function): no sanitizer report, and the same
-results as the regular build within fp64 rounding."""
+biased forward and rows, the bucket function), in both builds (double and
+single precision): no sanitizer report, and the same results as the regular
+build of the same precision within its rounding."""
 import os
 import shutil
 import subprocess
@@ -69,13 +70,15 @@ def _run_child(lib_path, npz, preload=None):
                           timeout=600)
 
 
-def test_oracle_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+@pytest.mark.parametrize("precision", ["fp64", "fp32"])
+def test_oracle_under_address_and_undefined_behaviour_sanitizers(tmp_path, precision):
     asan = _libasan()
     if shutil.which("gcc") is None or asan is None:
         pytest.skip("gcc with libasan needed")
-    plain = oracle.build(out=str(tmp_path / "liboracle_plain.so"))
+    mode = ["-DORACLE_FP32"] if precision == "fp32" else []
+    plain = oracle.build(out=str(tmp_path / "liboracle_plain.so"), extra_flags=mode)
     san = oracle.build(out=str(tmp_path / "liboracle_san.so"),
-                       extra_flags=["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                       extra_flags=[*mode, "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
                                     "-fno-omit-frame-pointer"])
     r_plain = _run_child(plain, str(tmp_path / "plain.npz"))
     assert r_plain.returncode == 0, r_plain.stderr[-3000:]
@@ -87,6 +90,7 @@ def test_oracle_under_address_and_undefined_behaviour_sanitizers(tmp_path):
     for k in a.files:
         x, y = a[k], b[k]
         if x.dtype.kind == "f":
-            assert np.allclose(x, y, rtol=1e-12, atol=1e-15, equal_nan=True), k
+            tol = dict(rtol=1e-12, atol=1e-15) if precision == "fp64" else dict(rtol=1e-6, atol=1e-9)
+            assert np.allclose(x, y, equal_nan=True, **tol), k
         else:
             assert np.array_equal(x, y), k
