@@ -385,3 +385,27 @@ def test_prepared_call_matches_binding(name):
             assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), i
         else:
             assert torch.equal(got, ref), i
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_most_groups_and_splits(softmax):
+    """The largest group count (one sequence in each of 64 groups, every group
+    with its own window, context, min-full tail and scale, the default scale
+    among them) through split-KV with the largest split count (128: most
+    chunks of the short sequences hold no key tile), then cross-attention over
+    8 192 keys in 128 splits of one 64-key tile each."""
+    from recsys_attention_amd import _abi
+    ng, ns = _abi.HSTU_MAX_GROUPS, _abi.HSTU_MAX_SPLITS
+    rng = np.random.default_rng(4242 + softmax)
+    groups = [W.MaskGroup(int(rng.choice([0, 1, 5, 40])), int(rng.choice([0, 2, 7])),
+                          int(rng.choice([0, 3, 30])), float(rng.choice([0.0, 1.0 / 128, 1.0 / 512])))
+              for _ in range(ng)]
+    w = W.build(f"groups{ng}_splits{ns}", dtype="bf16", batch=ng, nhead=2, hdim_qk=64, hdim_v=64,
+                jagged=True, cross=False, causal=True, softmax=softmax, alpha=0.0, groups=groups,
+                uih_q=rng.integers(0, 300, ng), targets=rng.integers(0, 6, ng), seed=4243 + softmax)
+    _check_full(w, num_splits=ns)
+    w = W.build(f"cross8192_splits{ns}", dtype="bf16", batch=2, nhead=2, hdim_qk=128, hdim_v=128,
+                jagged=True, cross=True, causal=True, softmax=softmax, alpha=0.0,
+                groups=[W.MaskGroup(0, 6, 0, 1.0 / 64)], uih_q=[64, 40], targets=[8, 3],
+                uih_kv=[8192 - 6, 5000], seed=4245 + softmax)
+    _check_full(w, num_splits=ns)
