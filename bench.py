@@ -10,8 +10,9 @@ the timed kernels; inputs are resident in HBM before timing starts.
 Prints one JSON line: effective TFLOP/s counting 2 * (hdim_qk + hdim_v) FLOPs
 per visible (b, h, i, j) pair over the median of the per-step HIP-event times
 (minimum, mean and the shader clock are logged beside it), the roofline of the
-dominant kernel, and the CPU oracle timed on a bounded sample of the same
-workload.
+dominant kernel (its own duration from events the library records around its
+launch, in a second loop of the same steps), and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -114,6 +115,29 @@ def timed_steps(torch, step, steps: int, warmup: int, warmup_s: float, stream):
     return med, rec
 
 
+def main_kernel_times(torch, call, steps: int, stream):
+    """Durations of the step's main kernel alone (the forward kernel, or the split
+    kernel of a split-KV step): a loop of its own after the timed one, in which the
+    library records one event pair per step right around that kernel's launch (the
+    argument block's profiling hooks), on the launch stream.  Returns the median
+    milliseconds and a record of the run."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for b, e in evs:  # an event exists once it has been recorded
+        b.record(stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    for b, e in evs:
+        call.set_profiling_events(b, e)
+        call()
+    call.set_profiling_events(None, None)
+    torch.cuda.synchronize()
+    per = sorted(b.elapsed_time(e) for b, e in evs)
+    med = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    return med, {"ms_median": round(med, 4), "ms_min": round(per[0], 4),
+                 "ms_mean": round(sum(per) / steps, 4), "ms_max": round(per[-1], 4)}
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -213,21 +237,30 @@ def algorithmic_bytes(w, rab=None) -> int:
     return b
 
 
-def roofline(w, splits, tflops, ms, traffic, rab=None):
-    """Roofline of the step's dominant kernel.  A workload with few query rows per
-    key (the split-KV cross-attention one: ~72 FLOP per byte, far below the
-    ~310 FLOP/B balance point of the chip) is bounded by HBM; then `achieved` is
-    the algorithmic bytes over the step time, which also holds the combine pass."""
+def roofline(w, splits, flops, ms, traffic, rab=None, kernel_ms=None):
+    """Roofline of the step's dominant kernel, the forward kernel (the split kernel
+    of a split-KV step): `achieved` is the step's algorithmic FLOPs or bytes over
+    that kernel's own median duration (kernel_ms, events the library records
+    around its launch), or over the whole step when that was not measured.  A
+    workload with few query rows per key (the split-KV cross-attention one: ~72
+    FLOP per byte, far below the ~310 FLOP/B balance point of the chip) is bounded
+    by HBM, the others by the MFMA."""
     peak = PEAK_TFLOPS[w.dtype]
-    flops_per_byte = (tflops * 1e12 * ms * 1e-3) / algorithmic_bytes(w, rab)
-    if flops_per_byte < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
-        gbs = algorithmic_bytes(w, rab) / (ms * 1e-3) / 1e9
+    t = kernel_ms if kernel_ms else ms
+    name = "hstu_fwd_kernel" + (f" (split, {splits} splits)" if splits > 1 else "")
+    covers = (f"{name} alone, HIP events around its launch" if kernel_ms else
+              "whole step" + (f" (split kernel + combine, {splits} splits)" if splits > 1 else ""))
+    nbytes = algorithmic_bytes(w, rab)
+    if flops / nbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gbs = nbytes / (t * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "covers": "whole step" + (f" (split kernel + combine, {splits} splits)" if splits > 1 else ""),
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel_ms": round(t, 4),
+                "covers": covers,
                 "traffic_unit": "bytes per launch of the forward kernel (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
+    tflops = flops / (t * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(tflops / peak, 4), "traffic": traffic,
+            "frac": round(tflops / peak, 4), "traffic": traffic, "kernel_ms": round(t, 4),
+            "covers": covers,
             "traffic_unit": "bytes per launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
 
 
@@ -428,6 +461,9 @@ def main():
 
     ms, timing = timed_steps(torch, step, args.steps, args.warmup, args.warmup_s, stream)
     timing["launch"] = args.launch
+    kernel_ms = None
+    if args.launch == "prepared":
+        kernel_ms, timing["main_kernel"] = main_kernel_times(torch, step, args.steps, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
@@ -449,7 +485,7 @@ def main():
                    "splits": splits, "schedule": args.schedule,
                    "schedule_run": schedule_run(w, splits, args.schedule),
                    "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)},
-        "roofline": roofline(w, splits, tflops, ms, traffic, rab),
+        "roofline": roofline(w, splits, flops, ms, traffic, rab, kernel_ms),
         "device": device_info(torch),
         "timing": timing,
     }

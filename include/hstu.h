@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 3
+#define HSTU_ABI_VERSION 4
 #define HSTU_MAX_GROUPS 64
 #define HSTU_MAX_SPLITS 128
 #define HSTU_RAB_TIME_BUCKETS 11 /* time-gap buckets of the relative attention bias */
@@ -135,6 +135,15 @@ typedef struct {
     const float *rab_time;         /* device [nhead][HSTU_RAB_TIME_BUCKETS], with rab_timestamps */
     const float *rab_pos;          /* device [nhead][rab_pos_len]; NULL = no positional term */
     int32_t rab_pos_len;           /* 1 ..= HSTU_RAB_MAX_POS when rab_pos is set */
+    /* Profiling hooks (ABI version 4), for callers that time the main kernel alone
+     * (the roofline of a benchmark): hipEvent_t handles, owned by the caller, that
+     * the call records on its stream right before and right after launching its
+     * main kernel (the forward kernel of hstu_fwd, the split kernel of
+     * hstu_fwd_splitkv); the planning and combine passes fall outside them.  Not
+     * recorded when the call launches nothing (an empty problem or an error).
+     * NULL = no event. */
+    void *prof_begin;
+    void *prof_end;
 } hstu_fwd_args_t;
 
 /* Host-only argument check (no HIP call); also run by every entry point.  It covers

@@ -88,7 +88,8 @@ hstu_status_t hstu_norm_gate_fwd(const hstu_norm_gate_args_t *args, void *hip_st
 /* One whole layer.  attn describes the sequences (batched or jagged), heads, head
  * dims, mask, groups and optional relative bias exactly as for hstu_fwd; it must
  * be self-attention (cross = 0) and its q, k, v, o, token strides and lse are
- * ignored (the layer uses its own buffers).  Tokens n = attn.total_q (jagged) or
+ * ignored (the layer uses its own buffers); its profiling events, when set,
+ * bracket the attention's forward kernel.  Tokens n = attn.total_q (jagged) or
  * batch * seqlen_q.  x, out [n][d_model] dense; w1 [2 H (dv + dqk)][d_model];
  * b1 [2 H (dv + dqk)]; w2 [d_model][H dv]; b2 [d_model]; ln_gamma, ln_beta [H dv]
  * or NULL.  d_model % 64 == 0; H dv a multiple of 64 (the input width of f2) and

@@ -317,6 +317,13 @@ class PreparedCall:
         self._return_lse = return_lse
         self._streams = {}
 
+    def set_profiling_events(self, begin=None, end=None):
+        """torch.cuda.Event objects (or None) that the following calls record right
+        before and right after their main kernel (the argument block's profiling
+        hooks); an event must have been recorded once, so that it exists."""
+        self._c.args.prof_begin = begin.cuda_event if begin is not None else None
+        self._c.args.prof_end = end.cuda_event if end is not None else None
+
     def __call__(self, stream=None):
         if stream is None:
             stream = torch.cuda.current_stream(self._c.device)

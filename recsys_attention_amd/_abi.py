@@ -20,7 +20,7 @@ HSTU_FP16 = 0
 HSTU_BF16 = 1
 HSTU_MAX_GROUPS = 64
 HSTU_MAX_SPLITS = 128
-HSTU_ABI_VERSION = 3
+HSTU_ABI_VERSION = 4
 HSTU_RAB_TIME_BUCKETS = 11
 HSTU_RAB_MAX_POS = 2048
 HSTU_NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -58,7 +58,8 @@ class FwdArgsC(ctypes.Structure):
                 ("groups", ctypes.POINTER(MaskGroupC)), ("lse", ctypes.c_void_p),
                 ("schedule", ctypes.c_int32),
                 ("rab_timestamps", ctypes.c_void_p), ("rab_time", ctypes.c_void_p),
-                ("rab_pos", ctypes.c_void_p), ("rab_pos_len", ctypes.c_int32)]
+                ("rab_pos", ctypes.c_void_p), ("rab_pos_len", ctypes.c_int32),
+                ("prof_begin", ctypes.c_void_p), ("prof_end", ctypes.c_void_p)]
 
 
 class LinearArgsC(ctypes.Structure):

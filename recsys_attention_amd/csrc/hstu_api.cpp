@@ -296,6 +296,14 @@ int64_t rows_q(const hstu_fwd_args_t *a) { return ::rows_q(a); }
 }  // namespace api
 }  // namespace hstu
 
+namespace {
+// the caller's profiling event (hstu_fwd_args_t::prof_begin / prof_end), if any
+hstu_status_t record_prof(void *ev, hipStream_t stream) {
+    if (ev == nullptr) return HSTU_OK;
+    return hip_status(hipEventRecord((hipEvent_t)ev, stream), "profiling event record");
+}
+}  // namespace
+
 extern "C" {
 
 hstu_status_t hstu_validate_args(const hstu_fwd_args_t *args) { return validate(args); }
@@ -333,8 +341,10 @@ hstu_status_t hstu_fwd(const hstu_fwd_args_t *args, void *ws, size_t ws_bytes, v
         if ((st = check_grid(p)) != HSTU_OK) return st;
     }
     hipStream_t stream = (hipStream_t)hip_stream;
+    if ((st = record_prof(args->prof_begin, stream)) != HSTU_OK) return st;
     st = hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, false, stream),
                     "forward kernel launch");
+    if (st == HSTU_OK) st = record_prof(args->prof_end, stream);
     if (st != HSTU_OK || !p.heavy) return st;
     return hip_status(hstu::launch_heavy_combine(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, stream),
                       "heavy q-tile combine launch");
@@ -362,8 +372,10 @@ hstu_status_t hstu_fwd_splitkv(const hstu_fwd_args_t *args, int32_t num_splits, 
     p.part_lse = args->softmax ? (float *)((char *)ws + ((rows * args->hdim_v * sizeof(float) + 255) / 256) * 256)
                                : nullptr;
     hipStream_t stream = (hipStream_t)hip_stream;
+    if ((st = record_prof(args->prof_begin, stream)) != HSTU_OK) return st;
     st = hip_status(hstu::launch_forward(p, args->dtype, args->hdim_qk, args->hdim_v, args->softmax != 0, true, stream),
                     "split-KV kernel launch");
+    if (st == HSTU_OK) st = record_prof(args->prof_end, stream);
     if (st != HSTU_OK) return st;
     return hip_status(hstu::launch_combine(p, args->dtype, args->hdim_v, args->softmax != 0, stream),
                       "combine kernel launch");
