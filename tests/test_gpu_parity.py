@@ -409,3 +409,34 @@ def test_most_groups_and_splits(softmax):
                 groups=[W.MaskGroup(0, 6, 0, 1.0 / 64)], uih_q=[64, 40], targets=[8, 3],
                 uih_kv=[8192 - 6, 5000], seed=4245 + softmax)
     _check_full(w, num_splits=ns)
+
+
+@pytest.mark.parametrize("name", ["jagged_silu_bf16_d128_local", "cross_softmax_lse_splitkv16_bf16_d128"])
+def test_profiling_events_bracket_the_main_kernel(name):
+    """The argument block's profiling hooks: the library records the caller's two
+    events around its main kernel (forward, or split-KV), inside the call's own
+    span, and the output is the same as without them."""
+    w = W.config(name)
+    dev = DeviceInputs(w)
+    call = dev.prepare(num_splits=w.num_splits)
+    _log(f"case {name}: profiling events")
+    ref = call()
+    ref = tuple(x.clone() for x in ref) if isinstance(ref, tuple) else ref.clone()
+    s = torch.cuda.current_stream()
+    b, e, t0, t1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    b.record(s)
+    e.record(s)
+    torch.cuda.synchronize()
+    t0.record(s)
+    call.set_profiling_events(b, e)
+    out = call()
+    call.set_profiling_events(None, None)
+    t1.record(s)
+    torch.cuda.synchronize()
+    if isinstance(out, tuple):
+        assert all(torch.equal(x, y) for x, y in zip(out, ref))
+    else:
+        assert torch.equal(out, ref)
+    k, step = b.elapsed_time(e), t0.elapsed_time(t1)
+    assert 0.0 < k <= step, (k, step)
+    assert t0.elapsed_time(b) >= 0.0 and e.elapsed_time(t1) >= 0.0
