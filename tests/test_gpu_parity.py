@@ -362,7 +362,8 @@ def test_heavy_qtiles_cut_into_chunks(case):
 
 
 @pytest.mark.parametrize("name", ["batched_silu_fp16_d64", "jagged_silu_bf16_d128_local",
-                                  "group4_silu_bf16_d256", "cross_softmax_lse_splitkv16_bf16_d128"])
+                                  "group4_silu_bf16_d256", "cross_softmax_lse_splitkv16_bf16_d128",
+                                  "jagged_silu_bf16_d128_causal_long"])
 def test_prepared_call_matches_binding(name):
     """hstu.prepare(): the argument block, output and workspace fixed once; every
     call (three in a row, then one on a side stream) gives bit for bit the output
